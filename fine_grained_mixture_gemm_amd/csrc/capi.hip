@@ -1,0 +1,402 @@
+// C ABI of libmoe: argument validation, workspace layout and the launch sequence of each entry point.
+// Every call validates synchronously, then enqueues kernels on the caller's stream; nothing is allocated.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MOE_TRY(x)                      \
+  do {                                  \
+    moe_status _s = (x);                \
+    if (_s != MOE_OK) return _s;        \
+  } while (0)
+
+// Tokens whose K-th and (K+1)-th fp32 keys differ by less than this are decided from fp64 logits.
+constexpr float kRecheckDelta = 1e-4f;
+
+bool use_mfma_gemm(const moe_config* c) { return c->w_dtype != MOE_F32; }
+bool use_mfma_router(const moe_config* c) {
+  return c->act_dtype == MOE_BF16 && c->d_model % 64 == 0 && (long long)c->T * c->n_routed >= (1LL << 20);
+}
+
+// expert outputs: bf16 for E4M3 experts (the combine payload), fp32 otherwise
+int esz_y(const moe_config* c) { return c->w_dtype == MOE_FP8_E4M3 ? 2 : 4; }
+
+moe_status check_cfg(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->T < 0 || c->d_model <= 0 || c->n_routed <= 0 || c->n_shared < 0 || c->top_k <= 0 || c->inter_dim <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "sizes must be positive (T >= 0): T=%d d=%d E=%d Ks=%d K=%d f=%d", c->T,
+                c->d_model, c->n_routed, c->n_shared, c->top_k, c->inter_dim);
+  if (c->top_k > c->n_routed) return fail(MOE_ERR_INVALID_ARG, "top_k=%d exceeds n_routed=%d", c->top_k, c->n_routed);
+  if (c->gate != MOE_GATE_SOFTMAX && c->gate != MOE_GATE_SIGMOID_BIAS) return fail(MOE_ERR_INVALID_ARG, "bad gate %d", c->gate);
+  if (c->renorm != 0 && c->renorm != 1) return fail(MOE_ERR_INVALID_ARG, "renorm must be 0 or 1");
+  if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "bad act_dtype %d", c->act_dtype);
+  if (c->w_dtype != MOE_F32 && c->w_dtype != MOE_BF16 && c->w_dtype != MOE_FP8_E4M3)
+    return fail(MOE_ERR_INVALID_ARG, "bad w_dtype %d", c->w_dtype);
+  if (c->n_routed > 256) return fail(MOE_ERR_UNSUPPORTED, "n_routed=%d > 256 (one wave holds at most 256 keys)", c->n_routed);
+  if (c->top_k > 16) return fail(MOE_ERR_UNSUPPORTED, "top_k=%d > 16", c->top_k);
+  const bool pair_ok = (c->act_dtype == MOE_F32 && c->w_dtype == MOE_F32) ||
+                       (c->act_dtype == MOE_BF16 && (c->w_dtype == MOE_BF16 || c->w_dtype == MOE_FP8_E4M3));
+  if (!pair_ok) return fail(MOE_ERR_UNSUPPORTED, "unsupported (act, weight) dtype pair (%d, %d)", c->act_dtype, c->w_dtype);
+  if (c->w_dtype != MOE_F32 && (c->d_model % 256 != 0 || c->inter_dim % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "bf16/fp8 experts need d %% 256 == 0 and f %% 128 == 0 (d=%d f=%d)", c->d_model,
+                c->inter_dim);
+  const long long rows = (long long)c->T * c->top_k;
+  if (rows >= (1LL << 31) || (long long)c->n_shared * c->inter_dim >= (1LL << 30))
+    return fail(MOE_ERR_UNSUPPORTED, "T*K or Ks*f too large");
+  // the matrix-core kernels address activations and one expert's weights with 32-bit byte offsets
+  const long long fs = (long long)c->n_shared * c->inter_dim;
+  const long long big = std::max({(long long)c->T * c->d_model * 2, rows * c->inter_dim * 2, (long long)c->T * fs * 2,
+                                  2LL * std::max((long long)c->inter_dim, fs) * c->d_model * 2});
+  if (c->w_dtype != MOE_F32 && big >= (1LL << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "an activation or expert weight array exceeds 4 GiB");
+  return MOE_OK;
+}
+
+struct Layout {
+  size_t z, z64, wg_split, recheck_count, recheck_list;
+  size_t chunk_counts, chunk_base, mt_prefix;
+  size_t uq, us, a_r, a_s, as_r, as_s;
+  size_t f_idx, f_w, f_counts, f_offsets, f_perm, f_rowof, f_yr, f_ys;
+  size_t total;
+};
+
+Layout layout(const moe_config* c) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  const size_t T = c->T, E = c->n_routed, K = c->top_k, d = c->d_model, f = c->inter_dim;
+  const size_t fs = (size_t)c->n_shared * f;
+  const size_t rows = T * K;
+  const bool fp8 = c->w_dtype == MOE_FP8_E4M3;
+  const size_t esz_a = c->w_dtype == MOE_F32 ? 4 : (c->w_dtype == MOE_BF16 ? 2 : 1);
+  L.z = take(T * E * 4);
+  L.z64 = take(T * E * 8);
+  L.wg_split = take(use_mfma_router(c) ? 3 * E * d * 2 : 0);
+  L.recheck_count = take(16);
+  L.recheck_list = take(T * 4);
+  const size_t nch = dispatch_chunks(c->T);
+  L.chunk_counts = take(nch * E * 4);
+  L.chunk_base = take(nch * E * 4);
+  L.mt_prefix = take((E + 1) * 4);
+  L.uq = take(fp8 ? T * d : 0);
+  L.us = take(fp8 ? T * (d / 128) * 4 : 0);
+  L.a_r = take(rows * f * esz_a);
+  L.a_s = take(T * fs * esz_a);
+  L.as_r = take(fp8 ? rows * (f / 128) * 4 : 0);
+  L.as_s = take(fp8 ? T * (fs / 128) * 4 : 0);
+  L.f_idx = take(rows * 4);
+  L.f_w = take(rows * 4);
+  L.f_counts = take(E * 4);
+  L.f_offsets = take((E + 1) * 4);
+  L.f_perm = take(rows * 4);
+  L.f_rowof = take(rows * 4);
+  L.f_yr = take(rows * d * esz_y(c));
+  L.f_ys = take(T * d * esz_y(c));
+  L.total = off + 256;   // room to align the caller's base pointer up to 256 bytes
+  return L;
+}
+
+moe_status check_ws(const moe_config* c, void* ws, size_t ws_bytes, uint8_t** base, Layout* L) {
+  *L = layout(c);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < L->total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L->total);
+  *base = reinterpret_cast<uint8_t*>(align_up(reinterpret_cast<uintptr_t>(ws), 256));
+  return MOE_OK;
+}
+
+int device_cus() {
+  static thread_local int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != cached_dev) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached_dev = dev;
+    cached_cus = n;
+  }
+  return cached_cus;
+}
+
+moe_status check_layer_router(const moe_layer* l) {
+  if (!l) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+  if (!l->w_gate) return fail(MOE_ERR_INVALID_ARG, "layer->w_gate is NULL");
+  return MOE_OK;
+}
+
+moe_status check_layer_experts(const moe_config* c, const moe_layer* l) {
+  if (!l) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+  if (!l->w13 || !l->w2) return fail(MOE_ERR_INVALID_ARG, "layer->w13 / w2 is NULL");
+  const bool fp8 = c->w_dtype == MOE_FP8_E4M3;
+  if (fp8 && (!l->w13_scale || !l->w2_scale)) return fail(MOE_ERR_INVALID_ARG, "fp8 weights need w13_scale and w2_scale");
+  if (c->n_shared > 0) {
+    if (!l->ws13 || !l->ws2) return fail(MOE_ERR_INVALID_ARG, "n_shared > 0 needs ws13 and ws2");
+    if (fp8 && (!l->ws13_scale || !l->ws2_scale)) return fail(MOE_ERR_INVALID_ARG, "fp8 shared weights need scales");
+  }
+  return MOE_OK;
+}
+
+moe_status do_route(const moe_config* c, const moe_layer* l, const void* u, const float* bias, int32_t* idx, float* w,
+                    uint8_t* base, const Layout& L, hipStream_t s) {
+  RouteArgs a{};
+  a.u = u;
+  a.u_bf16 = c->act_dtype == MOE_BF16;
+  a.use_mfma = use_mfma_router(c);
+  a.wg = l->w_gate;
+  a.off = l->logit_offset;
+  a.bias = c->gate == MOE_GATE_SIGMOID_BIAS ? bias : nullptr;
+  a.T = c->T;
+  a.E = c->n_routed;
+  a.d = c->d_model;
+  a.K = c->top_k;
+  a.gate = c->gate;
+  a.renorm = c->renorm;
+  a.delta = kRecheckDelta;
+  a.z = reinterpret_cast<float*>(base + L.z);
+  a.z64 = reinterpret_cast<double*>(base + L.z64);
+  a.wg_split = reinterpret_cast<uint16_t*>(base + L.wg_split);
+  a.recheck_count = reinterpret_cast<int*>(base + L.recheck_count);
+  a.recheck_list = reinterpret_cast<int*>(base + L.recheck_list);
+  a.topk_idx = idx;
+  a.topk_w = w;
+  return hip_status(launch_route(a, s), "router launch");
+}
+
+moe_status do_dispatch(const moe_config* c, const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* row_of, uint8_t* base, const Layout& L, hipStream_t s) {
+  DispatchArgs a{};
+  a.topk_idx = idx;
+  a.T = c->T;
+  a.E = c->n_routed;
+  a.K = c->top_k;
+  a.chunk_counts = reinterpret_cast<int32_t*>(base + L.chunk_counts);
+  a.chunk_base = reinterpret_cast<int32_t*>(base + L.chunk_base);
+  a.counts = counts;
+  a.offsets = offsets;
+  a.perm_src = perm;
+  a.row_of = row_of;
+  return hip_status(launch_dispatch(a, s), "dispatch launch");
+}
+
+moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const int32_t* offsets, const int32_t* perm,
+                  void* y_r, void* y_s, uint8_t* base, const Layout& L, hipStream_t s) {
+  if (c->T == 0) return MOE_OK;
+  const bool fp8 = c->w_dtype == MOE_FP8_E4M3;
+  const bool mfma = use_mfma_gemm(c);
+  const int bm = mfma ? gemm_mfma_bm() : gemm_simt_bm();
+  int32_t* mt_prefix = reinterpret_cast<int32_t*>(base + L.mt_prefix);
+  MOE_TRY(hip_status(launch_schedule(offsets, c->n_routed, bm, mt_prefix, s), "schedule launch"));
+  const int fs = c->n_shared * c->inter_dim;
+  GemmArgs g{};
+  g.E = c->n_routed;
+  g.T = c->T;
+  g.d = c->d_model;
+  g.f = c->inter_dim;
+  g.fs = fs;
+  g.offsets = offsets;
+  g.perm_src = perm;
+  g.mt_prefix = mt_prefix;
+  const uint8_t* xin = static_cast<const uint8_t*>(u);
+  const float* xs = nullptr;
+  if (fp8) {
+    MOE_TRY(hip_status(launch_quant_act(u, true, c->T, c->d_model, base + L.uq, reinterpret_cast<float*>(base + L.us), s),
+                       "activation quantization launch"));
+    xin = base + L.uq;
+    xs = reinterpret_cast<const float*>(base + L.us);
+  }
+  // gate/up + SwiGLU
+  g.w_routed = static_cast<const uint8_t*>(l->w13);
+  g.w_shared = static_cast<const uint8_t*>(l->ws13);
+  g.ws_routed = l->w13_scale;
+  g.ws_shared = l->ws13_scale;
+  g.x_routed = xin;
+  g.x_shared = xin;
+  g.xs_routed = xs;
+  g.xs_shared = xs;
+  g.out_routed = base + L.a_r;
+  g.out_shared = base + L.a_s;
+  g.out_scale_routed = reinterpret_cast<float*>(base + L.as_r);
+  g.out_scale_shared = reinterpret_cast<float*>(base + L.as_s);
+  const long long rows = (long long)c->T * c->top_k;
+  if (mfma) {
+    const int grid = device_cus() / 8 * 8;
+    MOE_TRY(hip_status(launch_gemm_mfma(g, fp8, true, grid, s), "gate/up GEMM launch"));
+  } else {
+    const int mt_bound = (int)((rows + bm - 1) / bm) + c->n_routed;
+    const int mt_s = fs > 0 ? cdiv(c->T, bm) : 0;
+    const int tiles = mt_bound * cdiv(c->inter_dim, 32) + mt_s * cdiv(fs, 32);
+    MOE_TRY(hip_status(launch_gemm_simt(g, true, tiles, s), "gate/up GEMM launch"));
+  }
+  // down
+  g.w_routed = static_cast<const uint8_t*>(l->w2);
+  g.w_shared = static_cast<const uint8_t*>(l->ws2);
+  g.ws_routed = l->w2_scale;
+  g.ws_shared = l->ws2_scale;
+  g.x_routed = base + L.a_r;
+  g.x_shared = base + L.a_s;
+  g.xs_routed = reinterpret_cast<const float*>(base + L.as_r);
+  g.xs_shared = reinterpret_cast<const float*>(base + L.as_s);
+  g.out_routed = static_cast<uint8_t*>(y_r);
+  g.out_shared = static_cast<uint8_t*>(y_s);
+  g.out_scale_routed = nullptr;
+  g.out_scale_shared = nullptr;
+  if (mfma) {
+    const int grid = device_cus() / 8 * 8;
+    MOE_TRY(hip_status(launch_gemm_mfma(g, fp8, false, grid, s), "down GEMM launch"));
+  } else {
+    const int mt_bound = (int)((rows + bm - 1) / bm) + c->n_routed;
+    const int mt_s = fs > 0 ? cdiv(c->T, bm) : 0;
+    const int nt = cdiv(c->d_model, 64);
+    MOE_TRY(hip_status(launch_gemm_simt(g, false, mt_bound * nt + mt_s * nt, s), "down GEMM launch"));
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  MOE_TRY(check_cfg(cfg));
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layout(cfg).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, const moe_layer* layer, const void* u, const float* bias, int32_t* topk_idx,
+                     float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_layer_router(layer));
+  if (cfg->T > 0 && (!u || !topk_idx || !topk_w)) return fail(MOE_ERR_INVALID_ARG, "u / topk_idx / topk_w is NULL");
+  uint8_t* base;
+  Layout L;
+  MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
+  if (cfg->T == 0) return MOE_OK;
+  return do_route(cfg, layer, u, bias, topk_idx, topk_w, base, L, stream);
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                        int32_t* perm_src, int32_t* row_of, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (!counts || !offsets) return fail(MOE_ERR_INVALID_ARG, "counts / offsets is NULL");
+  if (cfg->T > 0 && (!topk_idx || !perm_src || !row_of)) return fail(MOE_ERR_INVALID_ARG, "topk_idx / perm_src / row_of is NULL");
+  uint8_t* base;
+  Layout L;
+  MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
+  if (cfg->T == 0) {
+    MOE_TRY(hip_status(hipMemsetAsync(counts, 0, sizeof(int32_t) * cfg->n_routed, stream), "memset counts"));
+    return hip_status(hipMemsetAsync(offsets, 0, sizeof(int32_t) * (cfg->n_routed + 1), stream), "memset offsets");
+  }
+  return do_dispatch(cfg, topk_idx, counts, offsets, perm_src, row_of, base, L, stream);
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const moe_layer* layer, const void* u, const int32_t* offsets,
+                          const int32_t* perm_src, void* y_routed, void* y_shared, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_layer_experts(cfg, layer));
+  if (cfg->T > 0 && (!u || !offsets || !perm_src || !y_routed)) return fail(MOE_ERR_INVALID_ARG, "u / offsets / perm_src / y_routed is NULL");
+  if (cfg->T > 0 && cfg->n_shared > 0 && !y_shared) return fail(MOE_ERR_INVALID_ARG, "y_shared is NULL with n_shared > 0");
+  uint8_t* base;
+  Layout L;
+  MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
+  return do_ffn(cfg, layer, u, offsets, perm_src, y_routed, cfg->n_shared > 0 ? y_shared : nullptr, base, L, stream);
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* u, const void* y_routed, const void* y_shared,
+                       const int32_t* row_of, const float* topk_w, void* h, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->T == 0) return MOE_OK;
+  if (!u || !y_routed || !row_of || !topk_w || !h) return fail(MOE_ERR_INVALID_ARG, "combine pointer is NULL");
+  if (cfg->n_shared > 0 && !y_shared) return fail(MOE_ERR_INVALID_ARG, "y_shared is NULL with n_shared > 0");
+  const bool bf16 = cfg->act_dtype == MOE_BF16;
+  return hip_status(launch_combine(u, bf16, y_routed, cfg->n_shared > 0 ? y_shared : nullptr, esz_y(cfg) == 2, row_of,
+                                   topk_w, cfg->T, cfg->d_model, cfg->top_k, h, stream),
+                    "combine launch");
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_layer* layer, const void* u, const float* bias, void* h,
+                       int32_t* topk_idx, int32_t* counts, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_layer_router(layer));
+  MOE_TRY(check_layer_experts(cfg, layer));
+  if (cfg->T > 0 && (!u || !h)) return fail(MOE_ERR_INVALID_ARG, "u / h is NULL");
+  uint8_t* base;
+  Layout L;
+  MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(base + L.f_idx);
+  int32_t* cnt = counts ? counts : reinterpret_cast<int32_t*>(base + L.f_counts);
+  if (cfg->T == 0) {
+    if (counts) return hip_status(hipMemsetAsync(counts, 0, sizeof(int32_t) * cfg->n_routed, stream), "memset counts");
+    return MOE_OK;
+  }
+  float* w = reinterpret_cast<float*>(base + L.f_w);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.f_offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(base + L.f_perm);
+  int32_t* row_of = reinterpret_cast<int32_t*>(base + L.f_rowof);
+  void* yr = base + L.f_yr;
+  void* ys = cfg->n_shared > 0 ? static_cast<void*>(base + L.f_ys) : nullptr;
+  MOE_TRY(do_route(cfg, layer, u, bias, idx, w, base, L, stream));
+  MOE_TRY(do_dispatch(cfg, idx, cnt, offsets, perm, row_of, base, L, stream));
+  MOE_TRY(do_ffn(cfg, layer, u, offsets, perm, yr, ys, base, L, stream));
+  return hip_status(launch_combine(u, cfg->act_dtype == MOE_BF16, yr, ys, esz_y(cfg) == 2, row_of, w, cfg->T,
+                                   cfg->d_model, cfg->top_k, h, stream),
+                    "combine launch");
+}
+
+moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* bias, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (!counts || !bias) return fail(MOE_ERR_INVALID_ARG, "counts / bias is NULL");
+  return hip_status(launch_bias_update(counts, cfg->n_routed, (long long)cfg->T * cfg->top_k, gamma, bias, stream),
+                    "bias update launch");
+}
+
+moe_status moe_quantize_weights(const float* w, int32_t batch, int32_t rows, int32_t cols, uint8_t* q, float* scales,
+                                hipStream_t stream) {
+  if (batch < 0 || rows <= 0 || cols <= 0) return fail(MOE_ERR_INVALID_ARG, "bad sizes batch=%d rows=%d cols=%d", batch, rows, cols);
+  if (rows % 128 || cols % 128) return fail(MOE_ERR_UNSUPPORTED, "rows and cols must be multiples of 128");
+  if (batch > 65535 || rows / 128 > 65535) return fail(MOE_ERR_UNSUPPORTED, "too many blocks");
+  if (batch > 0 && (!w || !q || !scales)) return fail(MOE_ERR_INVALID_ARG, "w / q / scales is NULL");
+  return hip_status(launch_quant_weight(w, batch, rows, cols, q, scales, stream), "weight quantization launch");
+}
+
+moe_status moe_quantize_act(const void* x, int32_t x_dtype, int32_t rows, int32_t cols, uint8_t* q, float* scales,
+                            hipStream_t stream) {
+  if (rows < 0 || cols <= 0) return fail(MOE_ERR_INVALID_ARG, "bad sizes rows=%d cols=%d", rows, cols);
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "x_dtype must be F32 or BF16");
+  if (cols % 128) return fail(MOE_ERR_UNSUPPORTED, "cols must be a multiple of 128");
+  if (rows > 0 && (!x || !q || !scales)) return fail(MOE_ERR_INVALID_ARG, "x / q / scales is NULL");
+  return hip_status(launch_quant_act(x, x_dtype == MOE_BF16, rows, cols, q, scales, stream), "activation quantization launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal kernel launch interfaces of libmoe (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteArgs {
+  const void* u;
+  bool u_bf16;
+  bool use_mfma;
+  const float* wg;
+  const float* off;
+  const float* bias;
+  int T, E, d, K, gate, renorm;
+  float delta;
+  float* z;               // [T, E] fp32 logits
+  double* z64;            // [T, E] fp64 logits of rechecked tokens (compacted)
+  uint16_t* wg_split;     // [3, E, d] bf16 parts of w_gate (MFMA logits)
+  int* recheck_count;
+  int* recheck_list;      // [T]
+  int32_t* topk_idx;
+  float* topk_w;
+};
+
+struct DispatchArgs {
+  const int32_t* topk_idx;
+  int T, E, K;
+  int32_t* chunk_counts;  // [chunks, E]
+  int32_t* chunk_base;    // [chunks, E]
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm_src;
+  int32_t* row_of;
+};
+
+// One grouped GEMM launch (gate/up + SwiGLU, or down) over the E routed groups and the shared group.
+struct GemmArgs {
+  int E, T, d, f, fs;
+  const int32_t* offsets;
+  const int32_t* perm_src;
+  const int32_t* mt_prefix;   // [E+1] prefix of M tiles per routed expert
+  const uint8_t* w_routed;    // w13 or w2 of all routed experts
+  const uint8_t* w_shared;
+  const float* ws_routed;     // fp8 block scales
+  const float* ws_shared;
+  const uint8_t* x_routed;    // gate/up: u (gathered through perm_src); down: a rows
+  const uint8_t* x_shared;
+  const float* xs_routed;     // fp8 activation scales
+  const float* xs_shared;
+  uint8_t* out_routed;        // gate/up: a; down: y
+  uint8_t* out_shared;
+  float* out_scale_routed;    // gate/up fp8: scales of a
+  float* out_scale_shared;
+};
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+int dispatch_chunks(int T);
+hipError_t launch_quant_act(const void* x, bool x_bf16, int rows, int cols, uint8_t* q, float* scales, hipStream_t s);
+hipError_t launch_quant_weight(const float* w, int batch, int rows, int cols, uint8_t* q, float* scales, hipStream_t s);
+hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_prefix, hipStream_t s);
+int gemm_mfma_bm();
+hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s);
+int gemm_simt_bm();
+hipError_t launch_gemm_simt(const GemmArgs& a, bool gateup, int max_tiles, hipStream_t s);
+hipError_t launch_combine(const void* u, bool bf16, const void* y_routed, const void* y_shared, bool y_bf16,
+                          const int32_t* row_of, const float* topk_w, int T, int d, int K, void* h, hipStream_t s);
+hipError_t launch_bias_update(const int32_t* counts, int E, long long TK, float gamma, float* bias, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,441 @@
+// Router: gate logits, scores, top-K selection and gates.
+//
+// DeepSeek Technical Report: MoE Architecture, 2.3 (g = Softmax_i(u_t^T e_i), then Top-K) and 3.3
+// (s = Sigmoid(u_t^T e_i); expert i is selected when s_i + b_i is among the K largest keys, and its gate
+// is the raw s_i). Keys are compared in fp32; a token whose K-th and (K+1)-th keys are closer than
+// `delta` is selected again from fp64 logits, so the selected set is the exact top-K of the keys.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ fp32 logits (VALU tile GEMM)
+// z[t, e] = sum_k u[t, k] * wg[e, k] + off[e]; 64 tokens x 64 experts per block, 4 x 4 per thread.
+template <typename TU>
+__global__ __launch_bounds__(256) void router_logits_valu(const TU* __restrict__ u, const float* __restrict__ wg,
+                                                          const float* __restrict__ off, int T, int E, int d,
+                                                          float* __restrict__ z, int* __restrict__ recheck_count) {
+  __shared__ float As[32][68];
+  __shared__ float Bs[32][68];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *recheck_count = 0;
+  const int tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  const int lr = tid >> 2, lk = (tid & 3) * 8;
+  for (int k0 = 0; k0 < d; k0 += 32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + lk + i;
+      float a = 0.f, b = 0.f;
+      if (t0 + lr < T && k < d) {
+        if constexpr (sizeof(TU) == 2) a = bf16_to_f32(u[(size_t)(t0 + lr) * d + k]);
+        else a = u[(size_t)(t0 + lr) * d + k];
+      }
+      if (e0 + lr < E && k < d) b = wg[(size_t)(e0 + lr) * d + k];
+      As[lk + i][lr] = a;
+      Bs[lk + i][lr] = b;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[k][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[k][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) z[(size_t)t * E + e] = acc[i][j] + (off ? off[e] : 0.f);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32-accurate logits on MFMA
+// w_gate is split exactly into three bf16 parts, w = hi + mid + lo (hi and mid truncate, lo holds the
+// last 8 significant bits); bf16 x bf16 products are exact in fp32, so the three bf16 GEMMs
+// accumulated in fp32 give the fp32 product of the bf16 tokens with the fp32 centroids.
+__global__ __launch_bounds__(256) void router_split_wg(const float* __restrict__ wg, long long n,
+                                                       uint16_t* __restrict__ parts) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float w = wg[i];
+  const uint32_t hb = __float_as_uint(w) & 0xFFFF0000u;
+  const float r1 = w - __uint_as_float(hb);
+  const uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(mb);
+  parts[i] = (uint16_t)(hb >> 16);
+  parts[n + i] = (uint16_t)(mb >> 16);
+  parts[2 * n + i] = f32_to_bf16(r2);
+}
+
+// 128 tokens x 64 experts per block; wave w owns experts 16w..16w+15 against all 128 tokens.
+// Tokens are staged 64 elements (128 bytes) at a time in a double-buffered XOR-swizzled LDS tile;
+// the centroid parts stream from global memory into registers.
+__global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ u, const uint16_t* __restrict__ parts,
+                                                          const float* __restrict__ off, int T, int E, int d,
+                                                          float* __restrict__ z, int* __restrict__ recheck_count) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][128 * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * 128, e0 = blockIdx.y * 64;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *recheck_count = 0;
+  const size_t n = (size_t)E * d;
+  const int erow = min(e0 + 16 * wave + (lane & 15), E - 1);
+  const uint8_t* wp = reinterpret_cast<const uint8_t*>(parts + (size_t)erow * d) + 16 * (lane >> 4);
+  const uint8_t* ub = reinterpret_cast<const uint8_t*>(u);
+  uint32_t boff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int id16 = q * 256 + tid;
+    const int tok = min(t0 + (id16 >> 3), T - 1);
+    boff[q] = (uint32_t)tok * (uint32_t)d * 2u + (id16 & 7) * 16;
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nst = d / 64;
+  i32x4 Bst[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) Bst[q] = *reinterpret_cast<const i32x4*>(ub + boff[q]);
+  for (int kb = 0; kb < nst; ++kb) {
+    uint8_t* buf = lds[kb & 1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int id16 = q * 256 + tid, row = id16 >> 3, c = id16 & 7;
+      *reinterpret_cast<i32x4*>(buf + row * 128 + ((c ^ (row & 7)) * 16)) = Bst[q];
+    }
+    __syncthreads();
+    if (kb + 1 < nst) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Bst[q] = *reinterpret_cast<const i32x4*>(ub + (size_t)(kb + 1) * 128 + boff[q]);
+    }
+    i32x4 A[3][2];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const uint8_t* pp = wp + p * n * 2 + kb * 128;
+      A[p][0] = *reinterpret_cast<const i32x4*>(pp);
+      A[p][1] = *reinterpret_cast<const i32x4*>(pp + 64);
+    }
+    const int tr = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 16 * j + tr;
+      const i32x4 b0 = *reinterpret_cast<const i32x4*>(buf + row * 128 + ((g ^ (row & 7)) * 16));
+      const i32x4 b1 = *reinterpret_cast<const i32x4*>(buf + row * 128 + (((4 + g) ^ (row & 7)) * 16));
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[p][0]),
+                                                         __builtin_bit_cast(bf16x8, b0), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[p][1]),
+                                                         __builtin_bit_cast(bf16x8, b1), acc[j], 0, 0, 0);
+      }
+    }
+  }
+  // lane holds experts 16 wave + 4 (lane >> 4) + r for token 16 j + (lane & 15)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int t = t0 + 16 * j + (lane & 15);
+    if (t >= T) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = e0 + 16 * wave + 4 * (lane >> 4) + r;
+      if (e < E) z[(size_t)t * E + e] = acc[j][r] + (off ? off[e] : 0.f);
+    }
+  }
+}
+
+void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s) {
+  const long long n = (long long)a.E * a.d;
+  router_split_wg<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.wg, n, a.wg_split);
+  dim3 grid(cdiv(a.T, 128), cdiv(a.E, 64));
+  router_logits_mfma<<<grid, 256, 0, s>>>((const uint16_t*)a.u, a.wg_split, a.off, a.T, a.E, a.d, a.z, a.recheck_count);
+}
+
+// ------------------------------------------------------------------ top-K of one token per wave
+__device__ __forceinline__ float f32_unorder(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Lane r < K ends with the r-th selected expert in `my_e`; returns the gap between the K-th and the
+// (K+1)-th largest key (+inf when K == E). Ties go to the lower expert index: the packed value puts the
+// complemented index in the low word.
+__device__ __forceinline__ float wave_topk_f32(const float key[4], const bool valid[4], int E, int K, int lane,
+                                               int& my_e) {
+  uint64_t packed[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    packed[j] = valid[j] ? ((uint64_t)f32_order(key[j]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * j)) : 0;
+  float kth = 0.f, k1 = __builtin_inff();
+  const int rounds = K < E ? K + 1 : K;
+  my_e = -1;
+  for (int r = 0; r < rounds; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) best = packed[j] > best ? packed[j] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+    const float kv = f32_unorder((uint32_t)(best >> 32));
+    if ((e & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j == (e >> 6)) packed[j] = 0;
+    }
+    if (r < K && lane == r) my_e = e;
+    if (r == K - 1) kth = kv;
+    if (r == K) k1 = kv;
+  }
+  return kth - k1;
+}
+
+template <int GATE>
+__global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, int T, int E, int K,
+                                                   const float* __restrict__ bias, int renorm, float delta,
+                                                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                   int* __restrict__ recheck_count, int* __restrict__ recheck_list) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float zz[4], key[4], score[4];
+  bool valid[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    valid[j] = e < E;
+    zz[j] = valid[j] ? z[(size_t)t * E + e] : -__builtin_inff();
+  }
+  if (GATE == MOE_GATE_SOFTMAX) {
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, zz[j]);
+    m = wave_max(m);
+    float p[4], s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = valid[j] ? expf(zz[j] - m) : 0.f;
+      s += p[j];
+    }
+    s = wave_sum(s);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      score[j] = p[j] / s;
+      key[j] = zz[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      score[j] = valid[j] ? 1.0f / (1.0f + expf(-zz[j])) : 0.f;
+      key[j] = score[j] + ((bias && valid[j]) ? bias[e] : 0.f);
+    }
+  }
+  int my_e;
+  const float gap = wave_topk_f32(key, valid, E, K, lane, my_e);
+  // gate of this lane's expert: fetch score[my_e >> 6] from lane my_e & 63
+  const int src = my_e < 0 ? 0 : (my_e & 63);
+  float g = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float v = __shfl(score[j], src, 64);
+    if (my_e >= 0 && j == (my_e >> 6)) g = v;
+  }
+  if (renorm) g = g / wave_sum(lane < K ? g : 0.f);
+  // rank of this lane's expert among the K selected -> ascending order
+  int rank = 0;
+  for (int q = 0; q < K; ++q) {
+    const int eq = __shfl(my_e, q, 64);
+    rank += (eq < my_e) ? 1 : 0;
+  }
+  if (lane < K) {
+    topk_idx[(size_t)t * K + rank] = my_e;
+    topk_w[(size_t)t * K + rank] = g;
+  }
+  if (lane == 0 && gap < delta) {
+    const int pos = atomicAdd(recheck_count, 1);
+    recheck_list[pos] = t;
+  }
+}
+
+// ------------------------------------------------------------------ fp64 recheck of close tokens
+// Pass 1: fp64 logits of the flagged tokens. Work item = (group of 8 flagged tokens, 32 experts);
+// each wave owns 8 experts, lanes stride over d, products of the stored inputs are exact in fp64.
+constexpr int kRecheckTok = 8, kRecheckExp = 32;
+
+template <typename TU>
+__global__ __launch_bounds__(256) void router_recheck_logits(const TU* __restrict__ u, const float* __restrict__ wg,
+                                                             const float* __restrict__ off, int E, int d,
+                                                             const int* __restrict__ recheck_count,
+                                                             const int* __restrict__ recheck_list,
+                                                             double* __restrict__ z64) {
+  const int n = *recheck_count;
+  const int groups = cdiv(n, kRecheckTok), echunks = cdiv(E, kRecheckExp);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int item = blockIdx.x; item < groups * echunks; item += gridDim.x) {
+    const int g = item / echunks, ec = item % echunks;
+    int toks[kRecheckTok];
+    const int ntok = min(kRecheckTok, n - g * kRecheckTok);
+#pragma unroll
+    for (int i = 0; i < kRecheckTok; ++i) toks[i] = recheck_list[g * kRecheckTok + min(i, ntok - 1)];
+    for (int ee = 0; ee < kRecheckExp / 4; ++ee) {
+      const int e = ec * kRecheckExp + wave * (kRecheckExp / 4) + ee;
+      if (e >= E) break;
+      double acc[kRecheckTok] = {};
+      for (int k = lane; k < d; k += 64) {
+        const double w = (double)wg[(size_t)e * d + k];
+#pragma unroll
+        for (int i = 0; i < kRecheckTok; ++i) {
+          double x;
+          if constexpr (sizeof(TU) == 2) x = (double)bf16_to_f32(u[(size_t)toks[i] * d + k]);
+          else x = (double)u[(size_t)toks[i] * d + k];
+          acc[i] = fma(x, w, acc[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kRecheckTok; ++i) {
+        const double s = wave_sum(acc[i]);
+        if (lane == 0 && i < ntok) z64[(size_t)(g * kRecheckTok + i) * E + e] = s + (off ? (double)off[e] : 0.0);
+      }
+    }
+  }
+}
+
+// Pass 2: one wave per flagged token selects again from the fp64 logits and rewrites its outputs.
+template <int GATE>
+__global__ __launch_bounds__(256) void router_recheck_select(const double* __restrict__ z64, int E, int K,
+                                                             const float* __restrict__ bias, int renorm,
+                                                             const int* __restrict__ recheck_count,
+                                                             const int* __restrict__ recheck_list,
+                                                             int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  const int n = *recheck_count;
+  const int lane = threadIdx.x & 63;
+  for (int i = blockIdx.x * 4 + (threadIdx.x >> 6); i < n; i += gridDim.x * 4) {
+    const int t = recheck_list[i];
+    double zz[4], key[4], score[4];
+    bool valid[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      valid[j] = e < E;
+      zz[j] = valid[j] ? z64[(size_t)i * E + e] : -__builtin_inf();
+    }
+    if (GATE == MOE_GATE_SOFTMAX) {
+      double m = -__builtin_inf();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmax(m, zz[j]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
+      double p[4], s = 0.0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = valid[j] ? exp(zz[j] - m) : 0.0;
+        s += p[j];
+      }
+      s = wave_sum(s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        score[j] = p[j] / s;
+        key[j] = zz[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        score[j] = valid[j] ? 1.0 / (1.0 + exp(-zz[j])) : 0.0;
+        key[j] = score[j] + ((bias && valid[j]) ? (double)bias[e] : 0.0);
+      }
+    }
+    // K rounds of (key descending, index ascending) argmax over 64-bit ordered keys
+    uint64_t ok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ok[j] = valid[j] ? f64_order(key[j]) : 0;
+    int my_e = -1;
+    for (int r = 0; r < K; ++r) {
+      uint64_t best = 0;
+      int best_e = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        if (ok[j] > best || (ok[j] == best && ok[j] != 0 && e < best_e)) {
+          best = ok[j];
+          best_e = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t ob = __shfl_xor(best, o, 64);
+        const int oe = __shfl_xor(best_e, o, 64);
+        if (ob > best || (ob == best && oe < best_e)) {
+          best = ob;
+          best_e = oe;
+        }
+      }
+      if ((best_e & 63) == lane) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j == (best_e >> 6)) ok[j] = 0;
+      }
+      if (lane == r) my_e = best_e;
+    }
+    const int src = my_e < 0 ? 0 : (my_e & 63);
+    double g = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double v = __shfl(score[j], src, 64);
+      if (my_e >= 0 && j == (my_e >> 6)) g = v;
+    }
+    if (renorm) g = g / wave_sum(lane < K ? g : 0.0);
+    int rank = 0;
+    for (int q = 0; q < K; ++q) rank += (__shfl(my_e, q, 64) < my_e) ? 1 : 0;
+    if (lane < K) {
+      topk_idx[(size_t)t * K + rank] = my_e;
+      topk_w[(size_t)t * K + rank] = (float)g;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launcher
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  dim3 g1(cdiv(a.T, 64), cdiv(a.E, 64));
+  if (a.u_bf16) {
+    if (a.use_mfma) launch_router_logits_mfma(a, s);
+    else router_logits_valu<uint16_t><<<g1, 256, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.T, a.E, a.d, a.z, a.recheck_count);
+  } else {
+    router_logits_valu<float><<<g1, 256, 0, s>>>((const float*)a.u, a.wg, a.off, a.T, a.E, a.d, a.z, a.recheck_count);
+  }
+  const int nb = cdiv(a.T, 4);
+  if (a.gate == MOE_GATE_SOFTMAX)
+    router_topk<MOE_GATE_SOFTMAX><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.delta, a.topk_idx,
+                                                     a.topk_w, a.recheck_count, a.recheck_list);
+  else
+    router_topk<MOE_GATE_SIGMOID_BIAS><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.delta, a.topk_idx,
+                                                          a.topk_w, a.recheck_count, a.recheck_list);
+  const int grid = 256;
+  if (a.u_bf16)
+    router_recheck_logits<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.E, a.d,
+                                                         a.recheck_count, a.recheck_list, a.z64);
+  else
+    router_recheck_logits<float><<<grid, 256, 0, s>>>((const float*)a.u, a.wg, a.off, a.E, a.d, a.recheck_count,
+                                                      a.recheck_list, a.z64);
+  if (a.gate == MOE_GATE_SOFTMAX)
+    router_recheck_select<MOE_GATE_SOFTMAX><<<64, 256, 0, s>>>(a.z64, a.E, a.K, a.bias, a.renorm, a.recheck_count,
+                                                               a.recheck_list, a.topk_idx, a.topk_w);
+  else
+    router_recheck_select<MOE_GATE_SIGMOID_BIAS><<<64, 256, 0, s>>>(a.z64, a.E, a.K, a.bias, a.renorm,
+                                                                    a.recheck_count, a.recheck_list, a.topk_idx,
+                                                                    a.topk_w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

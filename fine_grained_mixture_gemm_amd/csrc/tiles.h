@@ -1,0 +1,54 @@
+// Tile list of one grouped GEMM launch: the routed experts in ascending order, each split into
+// M tiles of BM rows (mt_prefix[e] is the number of M tiles before expert e) times its N tiles with the
+// M index fastest, then the shared group over all T tokens.
+#pragma once
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+struct TileInfo {
+  int group;      // 0..E-1 routed, E shared
+  int n_tile;
+  int row0;       // first row of the tile within the group's rows
+  int nrows;      // valid rows (1..BM)
+  int rowbase;    // row of the tile's first row in the group's activation/output arrays
+};
+
+template <int BM>
+__device__ __forceinline__ TileInfo decode_tile(int id, const GemmArgs& a, int nt_r, int mt_routed) {
+  TileInfo ti;
+  const int32_t* __restrict__ mt_prefix = a.mt_prefix;
+  const int routed_tiles = mt_routed * nt_r;
+  if (id < routed_tiles) {
+    int lo = 0, hi = a.E;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (mt_prefix[mid] * nt_r <= id) lo = mid;
+      else hi = mid - 1;
+    }
+    const int e = lo;
+    const int p0 = mt_prefix[e];
+    const int mt = mt_prefix[e + 1] - p0;
+    const int local = id - p0 * nt_r;
+    ti.group = e;
+    ti.n_tile = local / mt;
+    const int m_tile = local - ti.n_tile * mt;
+    const int o0 = a.offsets[e], n_e = a.offsets[e + 1] - o0;
+    ti.row0 = m_tile * BM;
+    ti.nrows = min(BM, n_e - ti.row0);
+    ti.rowbase = o0 + ti.row0;
+  } else {
+    const int mt = cdiv(a.T, BM);
+    const int local = id - routed_tiles;
+    ti.group = a.E;
+    ti.n_tile = local / mt;
+    const int m_tile = local - ti.n_tile * mt;
+    ti.row0 = m_tile * BM;
+    ti.nrows = min(BM, a.T - ti.row0);
+    ti.rowbase = ti.row0;
+  }
+  return ti;
+}
+
+}  // namespace moe

@@ -1,0 +1,169 @@
+/*
+ * moe.h - C ABI of the DeepSeekMoE layer forward pass on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (DeepSeek Technical Report: MoE Architecture, 1.1 "Shared Expert Isolation" formula and
+ * 5.3 [1]) computes, for every token t with input row u_t:
+ *
+ *     h_t = u_t + sum_{i <= Ks} FFN_i(u_t) + sum_{i in TopK(t)} g_{i,t} FFN_i(u_t)
+ *
+ * with fine-grained routed SwiGLU experts FFN(x) = W2 (SiLU(W1 x) * (W3 x)) (DeepSeek-V3 walkthrough,
+ * "invariant core"), gates from a softmax over the routed experts (same report, 2.3) or from sigmoid
+ * affinities whose selection key carries a per-expert bias that never enters the gate (same report,
+ * 3.3 "Auxiliary-Loss-Free Load Balancing"), and optionally every expert GEMM in E4M3 with 1x128
+ * activation tiles, 128x128 weight blocks and FP32 accumulation promoted every 128 elements (same
+ * report, 3.6 "FP8 Mixed Precision Training").
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer argument is a DEVICE pointer unless marked "host". The caller owns every buffer;
+ *    the library allocates nothing. Scratch memory comes from a caller-provided workspace of at least
+ *    moe_workspace_size() bytes, 256-byte aligned.
+ *  - Calls validate their arguments synchronously (nothing is launched when they fail) and then enqueue
+ *    work on `stream` asynchronously. They never abort and never synchronize the device.
+ *  - Matrices are row-major. T = tokens, d = d_model, E = routed experts, Ks = shared experts,
+ *    K = routed experts per token, f = routed expert inner dim, fs = Ks * f. The Ks shared experts are
+ *    stored as one SwiGLU block of inner dim fs (concatenating the inner dims is the same as summing).
+ *  - Activations u and the output h have dtype act_dtype (F32 or BF16, bf16 = raw uint16 bits).
+ *  - Expert weights have dtype w_dtype. Supported (act, w) pairs: (F32, F32), (BF16, BF16),
+ *    (BF16, FP8_E4M3). bf16 and fp8 weights need d % 256 == 0 and f % 128 == 0.
+ *  - Expert outputs y (per routed row and shared) are BF16 for FP8_E4M3 weights (the combine payload of
+ *    the E4M3 design) and F32 otherwise.
+ *  - On a non-OK status, moe_last_error() returns a message for the calling thread.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null pointer, negative size, K > E, bad enum value */
+  MOE_ERR_UNSUPPORTED = 2,   /* valid but not implemented: dtype pair, E > 256, K > 16, tile alignment */
+  MOE_ERR_WORKSPACE = 3,     /* workspace missing or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4            /* a HIP launch or API call failed (message names it) */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Gating: softmax over the routed experts (DeepSeek Technical Report: MoE Architecture, 2.3), or
+ * sigmoid affinity with the selection-only bias (same report, 3.3). */
+typedef enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID_BIAS = 1 } moe_gate;
+
+typedef struct {
+  int32_t T;           /* tokens (>= 0; T == 0 is a no-op) */
+  int32_t d_model;     /* d */
+  int32_t n_routed;    /* E, 1..256 */
+  int32_t n_shared;    /* Ks, >= 0 */
+  int32_t top_k;       /* K, 1..min(E, 16) */
+  int32_t inter_dim;   /* f, inner dim of one routed expert (and of one shared expert) */
+  int32_t gate;        /* moe_gate */
+  int32_t renorm;      /* 1: gates divided by their sum over the selected experts */
+  int32_t act_dtype;   /* moe_dtype of u, h */
+  int32_t w_dtype;     /* moe_dtype of expert weights */
+} moe_config;
+
+/* Layer weights (device pointers, read only).
+ *  w13        [E, 2f, d]: rows 0..f-1 of each expert are W1 (gate), rows f..2f-1 are W3 (up).
+ *  w2         [E, d, f]: W2 (down).
+ *  w13_scale  [E, 2f/128, d/128] fp32, w2_scale [E, d/128, f/128] fp32: 128x128 block scales, fp8 only
+ *             (NULL otherwise); a stored weight w is the E4M3 value q times its block's scale.
+ *  ws13 [2fs, d], ws2 [d, fs] (+ ws13_scale [2fs/128, d/128], ws2_scale [d/128, fs/128]): the shared
+ *             experts as one block; NULL when Ks == 0.
+ *  w_gate     [E, d] fp32: the expert centroids e_i of the gate (logit z_{t,i} = u_t . e_i).
+ *  logit_offset [E] fp32 or NULL: added to every logit before gating (a fixed per-expert skew). */
+typedef struct {
+  const void* w13;
+  const void* w2;
+  const float* w13_scale;
+  const float* w2_scale;
+  const void* ws13;
+  const void* ws2;
+  const float* ws13_scale;
+  const float* ws2_scale;
+  const float* w_gate;
+  const float* logit_offset;
+} moe_layer;
+
+/* Bytes of workspace every call below needs for this configuration (host output). */
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Router: logits, gating and top-K (DeepSeek Technical Report: MoE Architecture, 2.3 gate formula;
+ * 3.3 and 5.3 [3]-[4] for sigmoid + bias).
+ *  u        [T, d] act_dtype.
+ *  bias     [E] fp32 selection bias, used only with MOE_GATE_SIGMOID_BIAS (NULL = zeros).
+ *  topk_idx [T, K] int32 out: the selected routed experts of each token in ascending expert order.
+ *           Keys are compared in fp32 and every token whose K-th and (K+1)-th keys are closer than
+ *           1e-4 is decided again from fp64 logits, so the set is the exact top-K; ties go to the
+ *           lower expert index.
+ *  topk_w   [T, K] fp32 out: gates, same order. Softmax: the probability over all E routed experts
+ *           (renormalised over the K selected when cfg->renorm). Sigmoid: the affinity s, never s + b
+ *           (renormalised when cfg->renorm). */
+moe_status moe_route(const moe_config* cfg, const moe_layer* layer, const void* u, const float* bias,
+                     int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch: expert histogram, exclusive prefix sum and permutation into expert-contiguous rows.
+ *  topk_idx [T, K] int32 in (as written by moe_route: distinct experts per token).
+ *  counts   [E] int32 out: tokens per routed expert (sums to T*K).
+ *  offsets  [E+1] int32 out: exclusive prefix sum of counts; rows of expert e are offsets[e]..offsets[e+1]-1.
+ *  perm_src [T*K] int32 out: token of each row; tokens ascend within an expert.
+ *  row_of   [T, K] int32 out: row of each (token, slot) pair, so perm_src[row_of[t][k]] == t. */
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                        int32_t* perm_src, int32_t* row_of, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert FFNs as grouped GEMMs: for every routed expert e and its rows (from moe_dispatch), and for
+ * the shared block over all T tokens, y = W2 (SiLU(W1 x) * (W3 x)).
+ * fp8 weights: x is quantized per row per 128 columns, each 128-element partial product is scaled
+ * and added into fp32 (DeepSeek Technical Report: MoE Architecture, 3.6), and SiLU(g) * v is
+ * quantized again per 128 columns before W2.
+ *  u         [T, d] act_dtype.   offsets [E+1], perm_src [T*K] from moe_dispatch.
+ *  y_routed  [T*K, d] out (BF16 for E4M3 weights, else F32), rows in dispatch order.
+ *  y_shared  [T, d] out, same dtype; NULL allowed only when Ks == 0. */
+moe_status moe_expert_ffn(const moe_config* cfg, const moe_layer* layer, const void* u, const int32_t* offsets,
+                          const int32_t* perm_src, void* y_routed, void* y_shared, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Combine: h_t = u_t + y_shared_t + sum_k topk_w[t][k] * y_routed[row_of[t][k]], summed in fp32 in
+ * that order (k ascending = expert ascending) and rounded once to act_dtype.
+ *  y_shared may be NULL when Ks == 0.  h [T, d] act_dtype out (must not alias the inputs). */
+moe_status moe_combine(const moe_config* cfg, const void* u, const void* y_routed, const void* y_shared,
+                       const int32_t* row_of, const float* topk_w, void* h, hipStream_t stream);
+
+/* The whole layer: moe_route, moe_dispatch, moe_expert_ffn and moe_combine on `stream`, with every
+ * intermediate in the workspace. topk_idx [T, K] and counts [E] are optional outputs (NULL to skip). */
+moe_status moe_forward(const moe_config* cfg, const moe_layer* layer, const void* u, const float* bias, void* h,
+                       int32_t* topk_idx, int32_t* counts, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bias update of auxiliary-loss-free balancing (DeepSeek Technical Report: MoE Architecture, 3.3):
+ * b_i <- b_i - gamma if expert i is overloaded, b_i + gamma if underloaded, where overloaded means
+ * counts[i] * E > T * K (load above the mean), underloaded the reverse; b_i is unchanged at the mean.
+ * One fp32 subtraction per expert, in place.  counts [E] int32, bias [E] fp32 in/out. */
+moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* bias,
+                           hipStream_t stream);
+
+/* Offline weight preparation (DeepSeek Technical Report: MoE Architecture, 3.6, 128x128 weight blocks):
+ * quantizes `batch` fp32 matrices w [batch, rows, cols] (rows, cols multiples of 128) to E4M3 codes
+ * q [batch, rows, cols] uint8 and block scales [batch, rows/128, cols/128] fp32 with
+ * s = amax/448, q = E4M3(w * (448/amax)) (nearest-even, saturating; s = 1 for an all-zero block). */
+moe_status moe_quantize_weights(const float* w, int32_t batch, int32_t rows, int32_t cols, uint8_t* q,
+                                float* scales, hipStream_t stream);
+
+/* Activation quantization, 1x128 tiles (same report, 3.6): x [rows, cols] of dtype x_dtype
+ * (F32 or BF16; cols % 128 == 0) -> q [rows, cols] E4M3 codes and scales [rows, cols/128] fp32, with the
+ * same scale rule as moe_quantize_weights. */
+moe_status moe_quantize_act(const void* x, int32_t x_dtype, int32_t rows, int32_t cols, uint8_t* q,
+                            float* scales, hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). Host string, owned by the
+ * library, valid until the next call on this thread. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */
