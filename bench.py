@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the DeepSeekMoE layer forward on one MI355X.
+
+One step = the whole hot path on one batch of seeded synthetic tokens: router (logits, gating, top-K),
+dispatch, the grouped expert GEMMs (gate/up + SwiGLU, down), combine, and the bias update when the
+workload has one. Inputs and weights are resident in HBM before timing starts. The default workload is
+the V3-shaped layer: T = 8192 tokens, d = 7168, 1 shared + 256 routed SwiGLU experts of inner dim 2048,
+sigmoid affinity + selection bias, top-8, renormalised gates, E4M3 experts with 1x128 / 128x128 scales.
+
+Prints ONE JSON line. `roofline` covers the dominant kernel (the gate/up grouped GEMM), timed live with
+HIP events on the launch stream over the timed steps; `cpu_baseline` times the float64 CPU oracle on a
+bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/sec + grouped-GEMM TFLOPS (% MFMA peak), V3-shaped layer, 1 GPU"
+PEAK = {"fp8": 5.0e15, "bf16": 2.5e15, "f32": 157.3e12, "hbm": 8.0e12}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_fp8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens of the workload the oracle runs")
+    return ap.parse_args()
+
+
+def kernel_work(w, counts):
+    """Algorithmic FLOPs and HBM bytes of the two grouped GEMM launches (each input and output once,
+    weights of the experts that received tokens)."""
+    touched = int((counts > 0).sum())
+    rows = w.T * w.K
+    ew = {"f32": 4, "bf16": 2, "fp8": 1}[w.wdt]
+    ex = 1 if w.wdt == "fp8" else (4 if w.act == "f32" else 2)     # activation bytes fed to gate/up
+    ea = {"f32": 4, "bf16": 2, "fp8": 1}[w.wdt]                       # SwiGLU output bytes
+    ey = 2 if w.wdt == "fp8" else 4                                    # expert output bytes
+    sc = 4 if w.wdt == "fp8" else 0
+    g = {
+        "flops": 2.0 * w.d * 2 * w.f * rows + 2.0 * w.d * 2 * w.fs * w.T,
+        "bytes": (touched * 2 * w.f * w.d * ew + touched * (2 * w.f // 128) * (w.d // 128) * sc
+                  + 2 * w.fs * w.d * ew + (2 * w.fs // 128) * (w.d // 128) * sc * (w.Ks > 0)
+                  + w.T * w.d * ex + w.T * (w.d // 128) * sc
+                  + (rows * w.f + w.T * w.fs) * ea + (rows * (w.f // 128) + w.T * (w.fs // 128)) * sc),
+    }
+    dn = {
+        "flops": 2.0 * w.f * w.d * rows + 2.0 * w.fs * w.d * w.T,
+        "bytes": (touched * w.d * w.f * ew + touched * (w.d // 128) * (w.f // 128) * sc
+                  + w.d * w.fs * ew + (w.d // 128) * (w.fs // 128) * sc * (w.Ks > 0)
+                  + (rows * w.f + w.T * w.fs) * ea + (rows * (w.f // 128) + w.T * (w.fs // 128)) * sc
+                  + (rows + w.T * (w.Ks > 0)) * w.d * ey),
+    }
+    return g, dn, touched
+
+
+def roofline(work, ms, peak_mfma):
+    t = ms * 1e-3
+    t_mfma = work["flops"] / peak_mfma
+    t_hbm = work["bytes"] / PEAK["hbm"]
+    if t_hbm >= t_mfma:
+        ach = work["bytes"] / t / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK["hbm"] / 1e9, "unit": "GB/s",
+                "frac": round(ach / (PEAK["hbm"] / 1e9), 4), "traffic": None}
+    ach = work["flops"] / t / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_mfma / 1e12, "unit": "TFLOP/s",
+            "frac": round(ach / (peak_mfma / 1e12), 4), "traffic": None}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def cpu_baseline(w, n_tokens):
+    """The float64 oracle on the first n_tokens tokens of the workload (their routed experts and the
+    shared block). Weight generation and E4M3 weight quantization are set-up and are not timed."""
+    import numpy as np
+    from oracle import moe as omoe, quant as oquant
+    from synth import configs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    ws = w.replace(T=n_tokens)
+    u = configs.u_as_f32(ws, configs.make_u(ws))
+    wg, bias, off = configs.make_router(ws)
+    r = omoe.route(omoe.router_logits(u, wg, off), ws.gate, ws.K, bias, ws.renorm)
+    need = sorted(set(int(e) for e in r["idx"].reshape(-1)))
+    experts = [None] * ws.E
+
+    def weights(e):
+        w1, w3, w2 = configs.master_w1(ws, e), configs.master_w3(ws, e), configs.master_w2(ws, e)
+        if ws.wdt == "fp8":
+            return (*oquant.quantize_weight_128x128(np.vstack([w1, w3])), *oquant.quantize_weight_128x128(w2))
+        if ws.wdt == "bf16":
+            from synth import gen
+            st = lambda x: gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(x))
+            return st(w1), st(w3), st(w2)
+        return w1, w3, w2
+
+    t0 = time.time()
+    for e in need:
+        experts[e] = weights(e)
+    shared = weights(-1) if ws.Ks > 0 else None
+    setup = time.time() - t0
+    runs, t_run = 0, 0.0
+    while runs < 3 and (runs == 0 or t_run < 10.0):
+        t1 = time.perf_counter()
+        omoe.layer_forward(u, wg, experts, shared, gate=ws.gate, K=ws.K, bias=bias, renorm=ws.renorm,
+                           logit_offset=off, fp8=(ws.wdt == "fp8"))
+        t_run += time.perf_counter() - t1
+        runs += 1
+    per = t_run / runs
+    return {"value": round(n_tokens / per, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"first {n_tokens} token(s) of the {w.name} workload through the float64 oracle layer "
+                       f"(their {len(need)} routed experts + the shared block), mean of {runs} run(s), "
+                       f"{per:.2f} s each; weight generation/quantization ({setup:.0f} s) untimed; "
+                       f"host: {cpu_model()}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this layer's multi-GPU "
+              f"sharding is a design note, not a code path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (HIP device)", file=sys.stderr)
+        sys.exit(1)
+    import fine_grained_mixture_gemm_amd as moe
+    from fine_grained_mixture_gemm_amd import layers
+    from synth import configs
+
+    w = configs.WORKLOADS[args.workload]
+    t_setup = time.time()
+    L = layers.device_layer(w)
+    setup_s = time.time() - t_setup
+    ws = torch.empty(moe.moe_workspace_size(L.cfg), dtype=torch.uint8, device="cuda")
+    h = torch.empty_like(L.t["u"])
+    idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    bias = L.t["bias"].clone() if L.t["bias"] is not None else None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_forward(L.cfg, L.layer, L.t["u"], bias, h, idx, counts, ws)
+        if w.gamma is not None:
+            moe.moe_update_bias(L.cfg, counts, w.gamma, bias)
+
+    # stage events: one set per timed step, created by recording them once
+    import ctypes
+    marks = []
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_MARKS)]
+        for e in evs:
+            e.record(stream)
+        marks.append(evs)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        arr = (ctypes.c_void_p * moe.MOE_NUM_MARKS)(*[e.cuda_event for e in marks[i]])
+        moe.moe_set_timing_events(arr)
+        step()
+    moe.moe_set_timing_events(None)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / args.steps
+    stage = {}
+    for a, b in zip(moe.MARK_NAMES[:-1], moe.MARK_NAMES[1:]):
+        ia, ib = moe.MARK_NAMES.index(a), moe.MARK_NAMES.index(b)
+        stage[b.replace("_end", "")] = sum(m[ia].elapsed_time(m[ib]) for m in marks) / args.steps
+    counts_h = counts.cpu().numpy()
+    gwork, dwork, touched = kernel_work(w, counts_h)
+    peak = PEAK[w.wdt]
+    gemm_ms = stage["gateup"] + stage["down"]
+    gemm_tflops = (gwork["flops"] + dwork["flops"]) / (gemm_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": {"fp8": "fp8_e4m3", "bf16": "bf16", "f32": "f32"}[w.wdt],
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d_model": w.d, "routed": w.E, "shared": w.Ks, "top_k": w.K,
+                   "inter_dim": w.f, "gate": w.gate, "renorm": w.renorm, "weights": w.wdt, "act": w.act,
+                   "bias_update": w.gamma is not None},
+        "roofline": dict(kernel="grouped_gemm_mfma gate/up+SwiGLU" if w.wdt != "f32" else "grouped_gemm_simt gate/up",
+                         **roofline(gwork, stage["gateup"], peak)),
+        "grouped_gemm_tflops": round(gemm_tflops, 1),
+        "grouped_gemm_mfma_frac": round(gemm_tflops * 1e12 / peak, 4),
+        "down_roofline": roofline(dwork, stage["down"], peak),
+        "stages_ms": {k: round(v, 4) for k, v in stage.items()},
+        "touched_experts": touched,
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,17 +15,19 @@ __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_GATE_SOFTMAX", "MOE_GATE_SIGMOID_BIAS", "MoeError",
     "moe_config", "moe_layer", "make_config", "make_layer", "moe_workspace_size", "moe_route", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_forward", "moe_update_bias", "moe_quantize_weights",
-    "moe_quantize_act", "moe_last_error", "LIB_PATH",
+    "moe_quantize_act", "moe_last_error", "moe_set_timing_events", "MOE_NUM_MARKS", "MARK_NAMES", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m fine_grained_mixture_gemm_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python fine_grained_mixture_gemm_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS = range(2)
+MARK_NAMES = ("route_begin", "route_end", "dispatch_end", "quant_end", "gateup_end", "down_end", "combine_end")
+MOE_NUM_MARKS = len(MARK_NAMES)
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
                 4: "MOE_ERR_HIP"}
 
@@ -58,6 +60,7 @@ _SIGS = {
     "moe_update_bias": [_CP, _vp, _f32, _vp, _vp],
     "moe_quantize_weights": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
     "moe_quantize_act": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
+    "moe_set_timing_events": [_vp, _i32],
 }
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
@@ -149,3 +152,11 @@ def moe_quantize_weights(w, q, scales, stream=None):
 def moe_quantize_act(x, x_dtype, q, scales, stream=None):
     rows, cols = x.shape
     _call("moe_quantize_act", _dev(x), x_dtype, rows, cols, _dev(q), _dev(scales), _stream(stream))
+
+
+def moe_set_timing_events(events):
+    """events: a ctypes array of MOE_NUM_MARKS hipEvent_t handles (host), or None to switch marks off."""
+    if events is None:
+        _call("moe_set_timing_events", None, 0)
+    else:
+        _call("moe_set_timing_events", ctypes.cast(events, ctypes.c_void_p), len(events))

@@ -1,5 +1,6 @@
 """Build the HIP libraries in-tree for gfx950: ``libmoe.so`` (the layer) and ``synth/libmoe_synth.so``
-(the device fill of synthetic inputs). Always recompiles. Usage: ``python -m fine_grained_mixture_gemm_amd.build``."""
+(the device fill of synthetic inputs). Always recompiles. Usage: ``python fine_grained_mixture_gemm_amd/build.py``
+(runs without importing the package, which needs the built library)."""
 from __future__ import annotations
 
 import concurrent.futures as cf

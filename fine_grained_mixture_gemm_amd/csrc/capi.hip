@@ -13,6 +13,12 @@ using namespace moe;
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t g_marks[MOE_NUM_MARKS];
+thread_local bool g_marks_on = false;
+
+void mark(int m, hipStream_t s) {
+  if (g_marks_on) (void)hipEventRecord(g_marks[m], s);
+}
 
 moe_status fail(moe_status s, const char* fmt, ...) {
   char buf[512];
@@ -187,7 +193,10 @@ moe_status do_route(const moe_config* c, const moe_layer* l, const void* u, cons
   a.recheck_list = reinterpret_cast<int*>(base + L.recheck_list);
   a.topk_idx = idx;
   a.topk_w = w;
-  return hip_status(launch_route(a, s), "router launch");
+  mark(MOE_MARK_ROUTE_BEGIN, s);
+  MOE_TRY(hip_status(launch_route(a, s), "router launch"));
+  mark(MOE_MARK_ROUTE_END, s);
+  return MOE_OK;
 }
 
 moe_status do_dispatch(const moe_config* c, const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* perm,
@@ -203,7 +212,9 @@ moe_status do_dispatch(const moe_config* c, const int32_t* idx, int32_t* counts,
   a.offsets = offsets;
   a.perm_src = perm;
   a.row_of = row_of;
-  return hip_status(launch_dispatch(a, s), "dispatch launch");
+  MOE_TRY(hip_status(launch_dispatch(a, s), "dispatch launch"));
+  mark(MOE_MARK_DISPATCH_END, s);
+  return MOE_OK;
 }
 
 moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const int32_t* offsets, const int32_t* perm,
@@ -232,6 +243,7 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
     xin = base + L.uq;
     xs = reinterpret_cast<const float*>(base + L.us);
   }
+  mark(MOE_MARK_QUANT_END, s);
   // gate/up + SwiGLU
   g.w_routed = static_cast<const uint8_t*>(l->w13);
   g.w_shared = static_cast<const uint8_t*>(l->ws13);
@@ -255,6 +267,7 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
     const int tiles = mt_bound * cdiv(c->inter_dim, 32) + mt_s * cdiv(fs, 32);
     MOE_TRY(hip_status(launch_gemm_simt(g, true, tiles, s), "gate/up GEMM launch"));
   }
+  mark(MOE_MARK_GATEUP_END, s);
   // down
   g.w_routed = static_cast<const uint8_t*>(l->w2);
   g.w_shared = static_cast<const uint8_t*>(l->ws2);
@@ -277,6 +290,7 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
     const int nt = cdiv(c->d_model, 64);
     MOE_TRY(hip_status(launch_gemm_simt(g, false, mt_bound * nt + mt_s * nt, s), "down GEMM launch"));
   }
+  mark(MOE_MARK_DOWN_END, s);
   return MOE_OK;
 }
 
@@ -285,6 +299,17 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
 extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_set_timing_events(hipEvent_t* events, int32_t n) {
+  if (!events || n == 0) {
+    g_marks_on = false;
+    return MOE_OK;
+  }
+  if (n < MOE_NUM_MARKS) return fail(MOE_ERR_INVALID_ARG, "need %d events, got %d", (int)MOE_NUM_MARKS, n);
+  for (int i = 0; i < MOE_NUM_MARKS; ++i) g_marks[i] = events[i];
+  g_marks_on = true;
+  return MOE_OK;
+}
 
 moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
   MOE_TRY(check_cfg(cfg));
@@ -340,9 +365,11 @@ moe_status moe_combine(const moe_config* cfg, const void* u, const void* y_route
   if (!u || !y_routed || !row_of || !topk_w || !h) return fail(MOE_ERR_INVALID_ARG, "combine pointer is NULL");
   if (cfg->n_shared > 0 && !y_shared) return fail(MOE_ERR_INVALID_ARG, "y_shared is NULL with n_shared > 0");
   const bool bf16 = cfg->act_dtype == MOE_BF16;
-  return hip_status(launch_combine(u, bf16, y_routed, cfg->n_shared > 0 ? y_shared : nullptr, esz_y(cfg) == 2, row_of,
-                                   topk_w, cfg->T, cfg->d_model, cfg->top_k, h, stream),
-                    "combine launch");
+  MOE_TRY(hip_status(launch_combine(u, bf16, y_routed, cfg->n_shared > 0 ? y_shared : nullptr, esz_y(cfg) == 2, row_of,
+                                    topk_w, cfg->T, cfg->d_model, cfg->top_k, h, stream),
+                     "combine launch"));
+  mark(MOE_MARK_COMBINE_END, stream);
+  return MOE_OK;
 }
 
 moe_status moe_forward(const moe_config* cfg, const moe_layer* layer, const void* u, const float* bias, void* h,
@@ -369,9 +396,11 @@ moe_status moe_forward(const moe_config* cfg, const moe_layer* layer, const void
   MOE_TRY(do_route(cfg, layer, u, bias, idx, w, base, L, stream));
   MOE_TRY(do_dispatch(cfg, idx, cnt, offsets, perm, row_of, base, L, stream));
   MOE_TRY(do_ffn(cfg, layer, u, offsets, perm, yr, ys, base, L, stream));
-  return hip_status(launch_combine(u, cfg->act_dtype == MOE_BF16, yr, ys, esz_y(cfg) == 2, row_of, w, cfg->T,
-                                   cfg->d_model, cfg->top_k, h, stream),
-                    "combine launch");
+  MOE_TRY(hip_status(launch_combine(u, cfg->act_dtype == MOE_BF16, yr, ys, esz_y(cfg) == 2, row_of, w, cfg->T,
+                                    cfg->d_model, cfg->top_k, h, stream),
+                     "combine launch"));
+  mark(MOE_MARK_COMBINE_END, stream);
+  return MOE_OK;
 }
 
 moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* bias, hipStream_t stream) {

@@ -158,6 +158,23 @@ moe_status moe_quantize_weights(const float* w, int32_t batch, int32_t rows, int
 moe_status moe_quantize_act(const void* x, int32_t x_dtype, int32_t rows, int32_t cols, uint8_t* q,
                             float* scales, hipStream_t stream);
 
+/* Stage marks for timing (a measurement aid, not part of the layer). After moe_set_timing_events(ev, n)
+ * with n >= MOE_NUM_MARKS, calls made on this thread record ev[m] on their stream at each mark m they pass:
+ * moe_forward records all of them; moe_route marks ROUTE_BEGIN..ROUTE_END, moe_dispatch DISPATCH_END,
+ * moe_expert_ffn QUANT_END..DOWN_END, moe_combine COMBINE_END. The events are created and owned by the
+ * caller (host handles); ev = NULL switches the marks off. Returns MOE_ERR_INVALID_ARG for 0 < n < NUM_MARKS. */
+typedef enum {
+  MOE_MARK_ROUTE_BEGIN = 0,  /* before the router kernels */
+  MOE_MARK_ROUTE_END,        /* after the router (topk_idx, topk_w ready) */
+  MOE_MARK_DISPATCH_END,     /* after histogram, scan and permutation */
+  MOE_MARK_QUANT_END,        /* after the tile schedule and (E4M3) the 1x128 activation quantization */
+  MOE_MARK_GATEUP_END,       /* after the gate/up + SwiGLU grouped GEMM */
+  MOE_MARK_DOWN_END,         /* after the down grouped GEMM */
+  MOE_MARK_COMBINE_END,      /* after the combine */
+  MOE_NUM_MARKS
+} moe_mark;
+moe_status moe_set_timing_events(hipEvent_t* events, int32_t n);
+
 /* Message for the last non-OK status returned on this thread ("" if none). Host string, owned by the
  * library, valid until the next call on this thread. */
 const char* moe_last_error(void);
