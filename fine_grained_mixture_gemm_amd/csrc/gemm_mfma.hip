@@ -13,87 +13,155 @@
 // Tile: 256 weight rows x 128 tokens, K staged 128 bytes at a time (128 E4M3 or 64 bf16 elements).
 // The product is formed transposed (weights as the MFMA A operand, tokens as B) so that each lane's
 // accumulators belong to one token: the token's scale is one value per lane and the 1x128 requant
-// reduces over channels held by the same lane. Eight waves: each owns 64 weight rows (for gate/up:
-// 32 gate channels and the same 32 up channels) against one half (64) of the tokens; weights stream
-// from HBM straight into registers, tokens go through a double-buffered, XOR-swizzled LDS tile.
-// The grid is persistent: blocks are split by XCD (block id mod 8) and each XCD walks one
-// contiguous range of the tile list, in which neighbouring tiles share an expert's weight tile.
+// reduces over channels held by the same lane. Four waves (one per SIMD) each own 64 weight rows (for
+// gate/up: 32 gate channels and the same 32 up channels) against all 128 tokens.
+// Operands move global -> LDS by the LDS-DMA loads (no registers), into a ring of three stages: two
+// stages are in flight while the third is multiplied, which covers the HBM latency of the weight
+// stream. LDS rows are XOR-swizzled in 16-byte chunks (chunk c of row r sits at c ^ (r & 7)), so the
+// MFMA operand reads are free of bank conflicts.
+// The grid is persistent: blocks are split by XCD (block id mod 8) and each XCD walks one contiguous
+// range of the tile list, in which neighbouring tiles share an expert's weight tile in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
 
 namespace moe {
 
-constexpr int kBM = 128;       // tokens per tile
-constexpr int kBW = 256;       // weight rows per tile
-constexpr int kStageB = 128;   // K bytes per stage
+constexpr int kBM = 128;        // tokens per tile
+constexpr int kBW = 256;        // weight rows per tile
+constexpr int kStageB = 128;    // K bytes per stage
 #ifndef MOE_GEMM_WM
 #define MOE_GEMM_WM 2
 #endif
-constexpr int kWM = MOE_GEMM_WM;          // token groups (waves along M)
-constexpr int kThreads = 256 * kWM;       // 4 weight-row groups x kWM token groups of waves
+constexpr int kWM = MOE_GEMM_WM;          // waves along the tokens (each takes 128 / kWM tokens)
+constexpr int kThreads = 256 * kWM;       // 4 weight-row groups x kWM token groups
 constexpr int kTJ = 8 / kWM;              // 16-token MFMA tiles per wave
-constexpr int kBQ = kBM * 8 / kThreads;   // 16-byte B chunks each thread stages per K step
+constexpr int kG = kThreads / 8;          // LDS rows covered by one pass of the loader
+constexpr int kStages = 3;      // LDS ring depth
+constexpr int kAChunks = kBW * 8 / kThreads;   // 16-byte A chunks each thread moves per stage (8)
+constexpr int kBChunks = kBM * 8 / kThreads;   // 16-byte B chunks each thread moves per stage (4)
+constexpr int kSlotA = kBW * kStageB;          // 32 KB
+constexpr int kSlotB = kBM * kStageB;          // 16 KB
+constexpr int kSlotS = kSlotA + kSlotB;          // token scales [128] then the two weight scales
+constexpr int kSlot = kSlotS + kBM * 4 + 16;
+constexpr int kLdsBytes = kStages * kSlot;
+static_assert(kLdsBytes >= kBM * 512 + 4 * kBM * 4, "the epilogue reuses the ring");
 
-template <bool FP8>
-__device__ __forceinline__ void mma_stage(f32x4 (&acc)[4][kTJ], const i32x4 (&A)[4][2], const uint8_t* __restrict__ lds_b,
-                                          const float* __restrict__ lds_sx, const float (&sw)[4], int lane, int tok0) {
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Global -> LDS copy of 16 (or 4) bytes per lane; the wave writes 64 consecutive pieces at `lds_base`.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 4, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 s_waitcnt fields:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]; expcnt and lgkmcnt left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// One K stage from an LDS slot. E4M3: each 16x16x128 product is a fresh partial sum that is scaled
+// and added into fp32; the products of token tile j+1 are issued before the additions of tile j so the
+// matrix core and the vector ALU work side by side.
+template <bool FP8, bool GATEUP>
+__device__ __forceinline__ void mma_stage(f32x4 (&acc)[4][kTJ], const uint8_t* __restrict__ slot, int wn, int tok0,
+                                          int lane) {
   const int tr = lane & 15, g = lane >> 4;
+  const uint8_t* A = slot;
+  const uint8_t* B = slot + kSlotA;
+  const float* SX = reinterpret_cast<const float*>(slot + kSlotS);
+  // this wave's four 16-row A tiles: gate/up LDS rows (i < 2 ? 0 : 128) + 32 wn + 16 (i & 1) (gate and
+  // up of the same channels); down LDS rows 64 wn + 16 i
+  i32x4 a[4][2];
 #pragma unroll
-  for (int j = 0; j < kTJ; ++j) {
+  for (int i = 0; i < 4; ++i) {
+    const int row = (GATEUP ? (i < 2 ? 0 : 128) + 32 * wn + 16 * (i & 1) : 64 * wn + 16 * i) + tr;
+    a[i][0] = *reinterpret_cast<const i32x4*>(A + row * kStageB + ((g ^ (row & 7)) * 16));
+    a[i][1] = *reinterpret_cast<const i32x4*>(A + row * kStageB + (((4 + g) ^ (row & 7)) * 16));
+  }
+  auto load_b = [&](int j, i32x4& b0, i32x4& b1) {
     const int row = tok0 + 16 * j + tr;
-    const int sw0 = ((g) ^ (row & 7)) * 16, sw1 = ((4 + g) ^ (row & 7)) * 16;
-    const i32x4 b0 = *reinterpret_cast<const i32x4*>(lds_b + row * kStageB + sw0);
-    const i32x4 b1 = *reinterpret_cast<const i32x4*>(lds_b + row * kStageB + sw1);
-    if constexpr (FP8) {
-      const float sx = lds_sx[row];
+    b0 = *reinterpret_cast<const i32x4*>(B + row * kStageB + ((g ^ (row & 7)) * 16));
+    b1 = *reinterpret_cast<const i32x4*>(B + row * kStageB + (((4 + g) ^ (row & 7)) * 16));
+  };
+  if constexpr (FP8) {
+    const float s0 = SX[kBM], s1 = SX[kBM + 1];             // weight block scales of this stage
+    float swi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) swi[i] = GATEUP ? (i < 2 ? s0 : s1) : (wn < 2 ? s0 : s1);
+    i32x8 aa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      aa[i] = i32x8{a[i][0][0], a[i][0][1], a[i][0][2], a[i][0][3], a[i][1][0], a[i][1][1], a[i][1][2], a[i][1][3]};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 p[2][4];
+    float sx[2];
+    {
+      i32x4 b0, b1;
+      load_b(0, b0, b1);
       const i32x8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const i32x8 aa = {A[i][0][0], A[i][0][1], A[i][0][2], A[i][0][3], A[i][1][0], A[i][1][1], A[i][1][2], A[i][1][3]};
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa, bb, zero, 0, 0, 0, 127, 0, 127);
-        const float sc = sx * sw[i];
+      for (int i = 0; i < 4; ++i) p[0][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa[i], bb, zero, 0, 0, 0, 127, 0, 127);
+      sx[0] = SX[tok0 + tr];
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, p[r], acc[i][j][r]);
+    for (int j = 0; j < kTJ; ++j) {
+      const int cur = j & 1, nxt = cur ^ 1;
+      if (j + 1 < kTJ) {
+        i32x4 b0, b1;
+        load_b(j + 1, b0, b1);
+        const i32x8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          p[nxt][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa[i], bb, zero, 0, 0, 0, 127, 0, 127);
+        sx[nxt] = SX[tok0 + 16 * (j + 1) + tr];
       }
-    } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[i][0]),
+        const float sc = sx[cur] * swi[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, p[cur][i][r], acc[i][j][r]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTJ; ++j) {
+      i32x4 b0, b1;
+      load_b(j, b0, b1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i][0]),
                                                             __builtin_bit_cast(bf16x8, b0), acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[i][1]),
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i][1]),
                                                             __builtin_bit_cast(bf16x8, b1), acc[i][j], 0, 0, 0);
       }
     }
   }
 }
 
-// LDS: two B stages (+ token scales) during the K loop; reused for the epilogue tile afterwards.
-constexpr int kLdsStage = kBM * kStageB + kBM * 4;
-constexpr int kLdsBytes = kBM * 512 + 4 * kBM * 4;   // >= 2 * kLdsStage; largest epilogue + amax table
-
 template <bool FP8, bool GATEUP>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
-  static_assert(kLdsBytes >= 2 * kLdsStage, "lds");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave & 3, wm = wave >> 2;   // weight-row group, token half (wave-uniform)
-  const int tok0 = 16 * kTJ * wm;
+  const int wn = wave & 3, wm = wave >> 2, tok0 = (128 / kWM) * wm;
   const int esz = FP8 ? 1 : 2;
-  const int32_t* __restrict__ mt_prefix = a.mt_prefix;
-  const int mt_routed = mt_prefix[a.E];
+  const int mt_routed = a.mt_prefix[a.E];
   const int fr = a.f, fs = a.fs;
   const int nt_r = GATEUP ? fr / 128 : a.d / kBW;
   const int nt_s = GATEUP ? fs / 128 : a.d / kBW;
   const int total = mt_routed * nt_r + (fs > 0 ? cdiv(a.T, kBM) * nt_s : 0);
 
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, slot_id = blockIdx.x >> 3, per = gridDim.x >> 3;
   const int chunk = cdiv(total, 8);
   const int t_begin = xcd * chunk, t_end = min(total, t_begin + chunk);
 
-  for (int id = t_begin + slot; id < t_end; id += per) {
+  for (int id = t_begin + slot_id; id < t_end; id += per) {
     const TileInfo ti = decode_tile<kBM>(id, a, nt_r, mt_routed);
     const bool shared = ti.group == a.E;
     const int fg = shared ? fs : fr;                       // inner dim of this group
@@ -101,7 +169,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
     const int kbytes = kelems * esz;
     const int nst = kbytes / kStageB;
     const int kblk = kelems / 128;                         // 128-element scale blocks along K
-    // ---- operand bases (uniform) and per-lane 32-bit offsets
     const uint8_t* __restrict__ W;
     const float* __restrict__ WS = nullptr;
     if (GATEUP) {
@@ -114,33 +181,43 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
     const uint8_t* __restrict__ X = shared ? a.x_shared : a.x_routed;
     const float* __restrict__ XS = FP8 ? (shared ? a.xs_shared : a.xs_routed) : nullptr;
     const int c0 = ti.n_tile * (GATEUP ? 128 : kBW);
-    // first weight row of each of this wave's four 16-row tiles (uniform)
-    int wrow0[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (GATEUP) wrow0[i] = (i < 2 ? c0 : fg + c0) + 32 * wn + 16 * (i & 1);
-      else wrow0[i] = c0 + 64 * wn + 16 * i;
-    }
-    uint32_t aoff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)(wrow0[i] + (lane & 15)) * kbytes + 16 * (lane >> 4);
-    // weight block-scale rows: gate/up tiles 0,1 share one 128-row block and 2,3 another; the down
-    // tiles all lie in one block
-    const float* __restrict__ wsA = FP8 ? WS + (size_t)(wrow0[0] / 128) * kblk : nullptr;
-    const float* __restrict__ wsB = FP8 ? WS + (size_t)(wrow0[2] / 128) * kblk : nullptr;
-    // ---- token rows this thread stages (2 x 16-byte chunks per stage) and its scale row
+
+    // ---- loader geometry. Thread tid moves, per stage, A chunks id = q*256 + tid (q < 8) and B chunks
+    // id = q*256 + tid (q < 4): LDS row id / 8, LDS position p = id % 8, holding global chunk p ^ (row & 7).
+    const int lrow = tid >> 3;                             // row within a kG-row group
+    const int lchunk = ((tid & 7) ^ (lrow & 7)) * 16;      // global chunk of this thread's LDS position
+    // LDS A row r = kG q + lrow holds weight row c0 + lrow + wrow(q), wrow wave-uniform:
+    //   gate/up: rows < 128 are W1 rows c0 + r, rows >= 128 are W3 rows fg + c0 + r - 128;
+    //   down:    W2 rows c0 + r.
+    const uint8_t* __restrict__ Wl = W + (size_t)(c0 + lrow) * kbytes + lchunk;
+    auto wrow_q = [&](int q) -> int {
+      const int r0 = kG * q;
+      return (GATEUP && r0 >= 128) ? fg + r0 - 128 : r0;
+    };
     auto src_row = [&](int r) -> int {
       const int rr = min(r, ti.nrows - 1);
       if (GATEUP) return shared ? ti.rowbase + rr : a.perm_src[ti.rowbase + rr];
       return ti.rowbase + rr;
     };
-    uint32_t boff[kBQ];
+    uint32_t boff[kBChunks];
 #pragma unroll
-    for (int q = 0; q < kBQ; ++q) {
-      const int id16 = q * kThreads + tid;
-      boff[q] = (uint32_t)src_row(id16 >> 3) * kbytes + (id16 & 7) * 16;
-    }
-    const uint32_t sxoff = (FP8 && tid < kBM) ? (uint32_t)src_row(tid) * kblk : 0u;
+    for (int q = 0; q < kBChunks; ++q) boff[q] = (uint32_t)src_row(q * kG + lrow) * kbytes + lchunk;
+    const uint32_t sxoff = (FP8 && wave < 2) ? (uint32_t)src_row(tid) * kblk : 0u;
+    // the tile's two weight block-scale rows: gate/up -> blocks c0/128 (gate) and (fg + c0)/128 (up);
+    // down -> blocks c0/128 (row groups 0, 1) and c0/128 + 1 (groups 2, 3). Lanes 0/1 of wave 2 copy them.
+    const float* wsrow = FP8 ? WS + (size_t)((lane == 0 ? c0 : (GATEUP ? fg + c0 : c0 + 128)) / 128) * kblk : nullptr;
+
+    auto issue = [&](int kb) {
+      uint8_t* slot = lds + (kb % kStages) * kSlot;
+      const uint8_t* Xk = X + (size_t)kb * kStageB;
+#pragma unroll
+      for (int q = 0; q < kAChunks; ++q)
+        dma16(Wl + ((size_t)wrow_q(q) * kbytes + (size_t)kb * kStageB), slot + (q * kThreads + wave * 64) * 16);
+#pragma unroll
+      for (int q = 0; q < kBChunks; ++q) dma16(Xk + boff[q], slot + kSlotA + (q * kThreads + wave * 64) * 16);
+      if (FP8 && wave < 2) dma4(XS + sxoff + kb, slot + kSlotS + wave * 256);
+      if (FP8 && wave == 2 && lane < 2) dma4(wsrow + kb, slot + kSlotS + kBM * 4);
+    };
 
     f32x4 acc[4][kTJ];
 #pragma unroll
@@ -148,62 +225,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < kTJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    i32x4 Acur[4][2], Anxt[4][2];
-    i32x4 Bst[kBQ];
-    float sxst = 0.f;
-    float swA_nxt = 1.f, swB_nxt = 1.f;
-    auto load_a = [&](i32x4 (&A)[4][2], int kb) {
-      const uint8_t* Wk = W + kb * kStageB;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        A[i][0] = *reinterpret_cast<const i32x4*>(Wk + aoff[i]);
-        A[i][1] = *reinterpret_cast<const i32x4*>(Wk + aoff[i] + 64);
-      }
-    };
-    auto load_b = [&](int kb) {
-      const uint8_t* Xk = X + kb * kStageB;
-#pragma unroll
-      for (int q = 0; q < kBQ; ++q) Bst[q] = *reinterpret_cast<const i32x4*>(Xk + boff[q]);
-      if (FP8 && tid < kBM) sxst = XS[sxoff + kb];
-    };
-    auto store_b = [&](int buf) {
-      uint8_t* base = lds + buf * kLdsStage;
-#pragma unroll
-      for (int q = 0; q < kBQ; ++q) {
-        const int id16 = q * kThreads + tid;
-        const int row = id16 >> 3, c = id16 & 7;
-        *reinterpret_cast<i32x4*>(base + row * kStageB + ((c ^ (row & 7)) * 16)) = Bst[q];
-      }
-      if (FP8 && tid < kBM) reinterpret_cast<float*>(base + kBM * kStageB)[tid] = sxst;
-    };
-    auto load_scales = [&](int kb) {
-      if constexpr (FP8) {
-        swA_nxt = wsA[kb];
-        swB_nxt = GATEUP ? wsB[kb] : swA_nxt;
-      }
-    };
-
-    load_b(0);
-    load_a(Acur, 0);
-    load_scales(0);
+    issue(0);
+    if (nst > 1) issue(1);
     for (int kb = 0; kb < nst; ++kb) {
-      uint8_t* buf = lds + (kb & 1) * kLdsStage;
-      store_b(kb & 1);
-      const float sw[4] = {swA_nxt, swA_nxt, swB_nxt, swB_nxt};
-      __syncthreads();
+      // stage kb landed (stage kb+1 may still be in flight), then every wave is past stage kb-1
       if (kb + 1 < nst) {
-        load_scales(kb + 1);
-        load_b(kb + 1);
-        load_a(Anxt, kb + 1);
+        if (FP8 && wave < 3) wait_vm<kAChunks + kBChunks + 1>();
+        else wait_vm<kAChunks + kBChunks>();
+      } else {
+        wait_vm<0>();
       }
-      mma_stage<FP8>(acc, Acur, buf, reinterpret_cast<const float*>(buf + kBM * kStageB), sw, lane, tok0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Acur[i][0] = Anxt[i][0];
-        Acur[i][1] = Anxt[i][1];
-      }
+      __builtin_amdgcn_s_barrier();
+      if (kb + 2 < nst) issue(kb + 2);
+      mma_stage<FP8, GATEUP>(acc, lds + (kb % kStages) * kSlot, wn, tok0, lane);
     }
-    __syncthreads();   // LDS is reused by the epilogue
+    __builtin_amdgcn_s_barrier();   // every wave is done with the ring before the epilogue reuses it
 
     // ---- epilogue. Lane holds, for token tok0 + 16j + (lane & 15), weight-row channels 4 (lane >> 4) + r
     // of each 16-row tile i.
@@ -317,19 +353,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
               *reinterpret_cast<const uint4*>(lds + row * 512 + c * 16);
       }
     }
-    __syncthreads();   // epilogue LDS reads finish before the next tile's stage 0 store
+    __syncthreads();   // epilogue LDS reads finish before the next tile's first DMA
   }
 }
 
 int gemm_mfma_bm() { return kBM; }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s) {
+  static bool attr_done[4] = {false, false, false, false};
+  const int k = (fp8 ? 2 : 0) + (gateup ? 1 : 0);
+  const void* fn = fp8 ? (gateup ? (const void*)grouped_gemm_mfma<true, true> : (const void*)grouped_gemm_mfma<true, false>)
+                       : (gateup ? (const void*)grouped_gemm_mfma<false, true> : (const void*)grouped_gemm_mfma<false, false>);
+  if (!attr_done[k]) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_done[k] = true;
+  }
   if (fp8) {
-    if (gateup) grouped_gemm_mfma<true, true><<<grid, kThreads, 0, s>>>(a);
-    else grouped_gemm_mfma<true, false><<<grid, kThreads, 0, s>>>(a);
+    if (gateup) grouped_gemm_mfma<true, true><<<grid, kThreads, kLdsBytes, s>>>(a);
+    else grouped_gemm_mfma<true, false><<<grid, kThreads, kLdsBytes, s>>>(a);
   } else {
-    if (gateup) grouped_gemm_mfma<false, true><<<grid, kThreads, 0, s>>>(a);
-    else grouped_gemm_mfma<false, false><<<grid, kThreads, 0, s>>>(a);
+    if (gateup) grouped_gemm_mfma<false, true><<<grid, kThreads, kLdsBytes, s>>>(a);
+    else grouped_gemm_mfma<false, false><<<grid, kThreads, kLdsBytes, s>>>(a);
   }
   return hipGetLastError();
 }
