@@ -13,12 +13,13 @@ import torch
 
 __all__ = [
     "MOE_F32", "MOE_BF16", "MOE_FP8_E4M3", "MOE_GATE_SOFTMAX", "MOE_GATE_SIGMOID_BIAS", "MoeError",
-    "moe_config", "moe_layer", "make_config", "make_layer", "moe_workspace_size", "moe_route", "moe_dispatch",
+    "moe_config", "moe_layer", "make_config", "make_layer", "moe_workspace_size", "moe_route", "moe_router_logits", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_forward", "moe_update_bias", "moe_quantize_weights",
     "moe_quantize_act", "moe_last_error", "moe_set_timing_events", "MOE_NUM_MARKS", "MARK_NAMES", "LIB_PATH",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# MOE_LIBRARY_PATH overrides the in-tree library (a developer switch for comparing builds).
+LIB_PATH = os.environ.get("MOE_LIBRARY_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python fine_grained_mixture_gemm_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
@@ -53,6 +54,7 @@ _CP, _LP = ctypes.POINTER(moe_config), ctypes.POINTER(moe_layer)
 _SIGS = {
     "moe_workspace_size": [_CP, ctypes.POINTER(_sz)],
     "moe_route": [_CP, _LP, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_router_logits": [_CP, _LP, _vp, _vp, _vp, _sz, _vp],
     "moe_dispatch": [_CP, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_expert_ffn": [_CP, _LP, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_combine": [_CP, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
@@ -116,6 +118,11 @@ def moe_workspace_size(cfg) -> int:
 def moe_route(cfg, layer, u, bias, topk_idx, topk_w, ws, stream=None):
     _call("moe_route", ctypes.byref(cfg), ctypes.byref(layer), _dev(u), _dev(bias), _dev(topk_idx), _dev(topk_w),
           _dev(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+
+
+def moe_router_logits(cfg, layer, u, z, ws, stream=None):
+    _call("moe_router_logits", ctypes.byref(cfg), ctypes.byref(layer), _dev(u), _dev(z), _dev(ws),
+          ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
 
 
 def moe_dispatch(cfg, topk_idx, counts, offsets, perm_src, row_of, ws, stream=None):

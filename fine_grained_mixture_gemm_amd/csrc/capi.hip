@@ -41,8 +41,11 @@ moe_status hip_status(hipError_t e, const char* what) {
     if (_s != MOE_OK) return _s;        \
   } while (0)
 
-// Tokens whose K-th and (K+1)-th fp32 keys differ by less than this are decided from fp64 logits.
-constexpr float kRecheckDelta = 1e-4f;
+// Tokens whose K-th and (K+1)-th fp32 keys differ by less than this are decided from fp64 logits. The
+// margins are at least 20x the largest fp32 key error measured against fp64 logits on the synthetic
+// layers: 1.7e-6 for sigmoid keys at d = 7168, 6.4e-6 for softmax keys (logits) at d = 1024.
+constexpr float kRecheckDeltaSigmoid = 4e-5f;
+constexpr float kRecheckDeltaSoftmax = 2e-4f;
 
 bool use_mfma_gemm(const moe_config* c) { return c->w_dtype != MOE_F32; }
 bool use_mfma_router(const moe_config* c) {
@@ -65,6 +68,7 @@ moe_status check_cfg(const moe_config* c) {
     return fail(MOE_ERR_INVALID_ARG, "bad w_dtype %d", c->w_dtype);
   if (c->n_routed > 256) return fail(MOE_ERR_UNSUPPORTED, "n_routed=%d > 256 (one wave holds at most 256 keys)", c->n_routed);
   if (c->top_k > 16) return fail(MOE_ERR_UNSUPPORTED, "top_k=%d > 16", c->top_k);
+  if (c->d_model > 8192) return fail(MOE_ERR_UNSUPPORTED, "d_model=%d > 8192 (fp64 router recheck)", c->d_model);
   const bool pair_ok = (c->act_dtype == MOE_F32 && c->w_dtype == MOE_F32) ||
                        (c->act_dtype == MOE_BF16 && (c->w_dtype == MOE_BF16 || c->w_dtype == MOE_FP8_E4M3));
   if (!pair_ok) return fail(MOE_ERR_UNSUPPORTED, "unsupported (act, weight) dtype pair (%d, %d)", c->act_dtype, c->w_dtype);
@@ -170,8 +174,8 @@ moe_status check_layer_experts(const moe_config* c, const moe_layer* l) {
   return MOE_OK;
 }
 
-moe_status do_route(const moe_config* c, const moe_layer* l, const void* u, const float* bias, int32_t* idx, float* w,
-                    uint8_t* base, const Layout& L, hipStream_t s) {
+RouteArgs route_args(const moe_config* c, const moe_layer* l, const void* u, const float* bias, int32_t* idx, float* w,
+                     uint8_t* base, const Layout& L) {
   RouteArgs a{};
   a.u = u;
   a.u_bf16 = c->act_dtype == MOE_BF16;
@@ -185,7 +189,7 @@ moe_status do_route(const moe_config* c, const moe_layer* l, const void* u, cons
   a.K = c->top_k;
   a.gate = c->gate;
   a.renorm = c->renorm;
-  a.delta = kRecheckDelta;
+  a.delta = c->gate == MOE_GATE_SOFTMAX ? kRecheckDeltaSoftmax : kRecheckDeltaSigmoid;
   a.z = reinterpret_cast<float*>(base + L.z);
   a.z64 = reinterpret_cast<double*>(base + L.z64);
   a.wg_split = reinterpret_cast<uint16_t*>(base + L.wg_split);
@@ -193,6 +197,12 @@ moe_status do_route(const moe_config* c, const moe_layer* l, const void* u, cons
   a.recheck_list = reinterpret_cast<int*>(base + L.recheck_list);
   a.topk_idx = idx;
   a.topk_w = w;
+  return a;
+}
+
+moe_status do_route(const moe_config* c, const moe_layer* l, const void* u, const float* bias, int32_t* idx, float* w,
+                    uint8_t* base, const Layout& L, hipStream_t s) {
+  const RouteArgs a = route_args(c, l, u, bias, idx, w, base, L);
   mark(MOE_MARK_ROUTE_BEGIN, s);
   MOE_TRY(hip_status(launch_route(a, s), "router launch"));
   mark(MOE_MARK_ROUTE_END, s);
@@ -328,6 +338,19 @@ moe_status moe_route(const moe_config* cfg, const moe_layer* layer, const void* 
   MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
   if (cfg->T == 0) return MOE_OK;
   return do_route(cfg, layer, u, bias, topk_idx, topk_w, base, L, stream);
+}
+
+moe_status moe_router_logits(const moe_config* cfg, const moe_layer* layer, const void* u, float* z, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_layer_router(layer));
+  if (cfg->T > 0 && (!u || !z)) return fail(MOE_ERR_INVALID_ARG, "u / z is NULL");
+  uint8_t* base;
+  Layout L;
+  MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
+  RouteArgs a = route_args(cfg, layer, u, nullptr, nullptr, nullptr, base, L);
+  a.z = z;
+  return hip_status(launch_router_logits(a, stream), "router logits launch");
 }
 
 moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,

@@ -55,6 +55,7 @@ struct GemmArgs {
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s);
 void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 int dispatch_chunks(int T);

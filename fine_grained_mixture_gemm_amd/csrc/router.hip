@@ -9,8 +9,10 @@
 
 namespace moe {
 
-// ------------------------------------------------------------------ fp32 logits (VALU tile GEMM)
+// ------------------------------------------------------------------ logits on the vector ALUs
 // z[t, e] = sum_k u[t, k] * wg[e, k] + off[e]; 64 tokens x 64 experts per block, 4 x 4 per thread.
+// The products of fp32 / bf16 inputs are exact in fp64 and accumulate in fp64 (same vector rate as
+// unpacked fp32); z is rounded to fp32 once.
 template <typename TU>
 __global__ __launch_bounds__(256) void router_logits_valu(const TU* __restrict__ u, const float* __restrict__ wg,
                                                           const float* __restrict__ off, int T, int E, int d,
@@ -21,7 +23,7 @@ __global__ __launch_bounds__(256) void router_logits_valu(const TU* __restrict__
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
   if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *recheck_count = 0;
   const int tx = tid & 15, ty = tid >> 4;
-  float acc[4][4] = {};
+  double acc[4][4] = {};
   const int lr = tid >> 2, lk = (tid & 3) * 8;
   for (int k0 = 0; k0 < d; k0 += 32) {
 #pragma unroll
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(256) void router_logits_valu(const TU* __restrict__
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma((double)a[i], (double)b[j], acc[i][j]);
     }
     __syncthreads();
   }
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(256) void router_logits_valu(const TU* __restrict__
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + tx * 4 + j;
-      if (e < E) z[(size_t)t * E + e] = acc[i][j] + (off ? off[e] : 0.f);
+      if (e < E) z[(size_t)t * E + e] = (float)(acc[i][j] + (off ? (double)off[e] : 0.0));
     }
   }
 }
@@ -268,44 +270,78 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, 
 }
 
 // ------------------------------------------------------------------ fp64 recheck of close tokens
-// Pass 1: fp64 logits of the flagged tokens. Work item = (group of 8 flagged tokens, 32 experts);
-// each wave owns 8 experts, lanes stride over d, products of the stored inputs are exact in fp64.
-constexpr int kRecheckTok = 8, kRecheckExp = 32;
+// Pass 1: fp64 logits of the flagged tokens. One block per routed expert e holds centroid row e in
+// registers (each thread every 256th element, as fp64), then takes the flagged tokens 8 at a time: their
+// u rows are copied into LDS with wide loads (all in flight together) and each of the 8 dot products is
+// reduced in fp64. Products of the stored inputs are exact in fp64.
+constexpr int kRecheckThreads = 256;
+constexpr int kRecheckMaxD = 8192;
+constexpr int kRecheckPer = kRecheckMaxD / kRecheckThreads;   // centroid elements per thread (32)
+constexpr int kRecheckBatch = 8;                               // flagged tokens per pass
 
 template <typename TU>
-__global__ __launch_bounds__(256) void router_recheck_logits(const TU* __restrict__ u, const float* __restrict__ wg,
-                                                             const float* __restrict__ off, int E, int d,
-                                                             const int* __restrict__ recheck_count,
-                                                             const int* __restrict__ recheck_list,
-                                                             double* __restrict__ z64) {
+__global__ __launch_bounds__(kRecheckThreads) void router_recheck_logits(const TU* __restrict__ u,
+                                                                         const float* __restrict__ wg,
+                                                                         const float* __restrict__ off, int E, int d,
+                                                                         const int* __restrict__ recheck_count,
+                                                                         const int* __restrict__ recheck_list,
+                                                                         double* __restrict__ z64) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t rl_lds[];   // [kRecheckBatch][d] of TU
+  __shared__ double part[kRecheckBatch][kRecheckThreads / 64];
   const int n = *recheck_count;
-  const int groups = cdiv(n, kRecheckTok), echunks = cdiv(E, kRecheckExp);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int item = blockIdx.x; item < groups * echunks; item += gridDim.x) {
-    const int g = item / echunks, ec = item % echunks;
-    int toks[kRecheckTok];
-    const int ntok = min(kRecheckTok, n - g * kRecheckTok);
+  if (n == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  TU* urows = reinterpret_cast<TU*>(rl_lds);
+  constexpr int V = 16 / sizeof(TU);                    // elements per 16-byte copy
+  for (int e = blockIdx.x; e < E; e += gridDim.x) {
+    double w[kRecheckPer];
 #pragma unroll
-    for (int i = 0; i < kRecheckTok; ++i) toks[i] = recheck_list[g * kRecheckTok + min(i, ntok - 1)];
-    for (int ee = 0; ee < kRecheckExp / 4; ++ee) {
-      const int e = ec * kRecheckExp + wave * (kRecheckExp / 4) + ee;
-      if (e >= E) break;
-      double acc[kRecheckTok] = {};
-      for (int k = lane; k < d; k += 64) {
-        const double w = (double)wg[(size_t)e * d + k];
+    for (int i = 0; i < kRecheckPer; ++i) {
+      const int k = tid + kRecheckThreads * i;
+      w[i] = k < d ? (double)wg[(size_t)e * d + k] : 0.0;
+    }
+    const double o = off ? (double)off[e] : 0.0;
+    for (int q0 = 0; q0 < n; q0 += kRecheckBatch) {
+      const int nb = min(kRecheckBatch, n - q0);
+      __syncthreads();                                  // previous batch's LDS reads are done
+      if (d % V == 0) {                                 // rows stay 16-byte aligned
+        for (int c = tid; c < nb * (d / V); c += kRecheckThreads) {
+          const int b = c / (d / V), k = (c % (d / V)) * V;
+          *reinterpret_cast<int4*>(urows + (size_t)b * d + k) =
+              *reinterpret_cast<const int4*>(u + (size_t)recheck_list[q0 + b] * d + k);
+        }
+      } else {
+        for (int c = tid; c < nb * d; c += kRecheckThreads) {
+          const int b = c / d, k = c % d;
+          urows[(size_t)b * d + k] = u[(size_t)recheck_list[q0 + b] * d + k];
+        }
+      }
+      __syncthreads();
+      double acc[kRecheckBatch];
 #pragma unroll
-        for (int i = 0; i < kRecheckTok; ++i) {
-          double x;
-          if constexpr (sizeof(TU) == 2) x = (double)bf16_to_f32(u[(size_t)toks[i] * d + k]);
-          else x = (double)u[(size_t)toks[i] * d + k];
-          acc[i] = fma(x, w, acc[i]);
+      for (int b = 0; b < kRecheckBatch; ++b) acc[b] = 0.0;
+#pragma unroll
+      for (int i = 0; i < kRecheckPer; ++i) {
+        const int k = tid + kRecheckThreads * i;
+        if (k < d) {
+#pragma unroll
+          for (int b = 0; b < kRecheckBatch; ++b) {
+            if (b < nb) {
+              double x;
+              if constexpr (sizeof(TU) == 2) x = (double)bf16_to_f32(urows[(size_t)b * d + k]);
+              else x = (double)urows[(size_t)b * d + k];
+              acc[b] = fma(x, w[i], acc[b]);
+            }
+          }
         }
       }
 #pragma unroll
-      for (int i = 0; i < kRecheckTok; ++i) {
-        const double s = wave_sum(acc[i]);
-        if (lane == 0 && i < ntok) z64[(size_t)(g * kRecheckTok + i) * E + e] = s + (off ? (double)off[e] : 0.0);
+      for (int b = 0; b < kRecheckBatch; ++b) {
+        const double sum = wave_sum(acc[b]);
+        if (lane == 0) part[b][wave] = sum;
       }
+      __syncthreads();
+      if (tid < nb) z64[(size_t)(q0 + tid) * E + e] = ((part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3])) + o;
     }
   }
 }
@@ -404,8 +440,8 @@ __global__ __launch_bounds__(256) void router_recheck_select(const double* __res
   }
 }
 
-// ------------------------------------------------------------------ launcher
-hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+// ------------------------------------------------------------------ launchers
+hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   dim3 g1(cdiv(a.T, 64), cdiv(a.E, 64));
   if (a.u_bf16) {
@@ -414,6 +450,13 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   } else {
     router_logits_valu<float><<<g1, 256, 0, s>>>((const float*)a.u, a.wg, a.off, a.T, a.E, a.d, a.z, a.recheck_count);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  hipError_t err = launch_router_logits(a, s);
+  if (err != hipSuccess) return err;
   const int nb = cdiv(a.T, 4);
   if (a.gate == MOE_GATE_SOFTMAX)
     router_topk<MOE_GATE_SOFTMAX><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.delta, a.topk_idx,
@@ -421,13 +464,18 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   else
     router_topk<MOE_GATE_SIGMOID_BIAS><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.delta, a.topk_idx,
                                                           a.topk_w, a.recheck_count, a.recheck_list);
-  const int grid = 256;
-  if (a.u_bf16)
-    router_recheck_logits<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.E, a.d,
-                                                         a.recheck_count, a.recheck_list, a.z64);
-  else
-    router_recheck_logits<float><<<grid, 256, 0, s>>>((const float*)a.u, a.wg, a.off, a.E, a.d, a.recheck_count,
-                                                      a.recheck_list, a.z64);
+  const size_t rl_bytes = (size_t)kRecheckBatch * a.d * (a.u_bf16 ? 2 : 4);
+  if (a.u_bf16) {
+    (void)hipFuncSetAttribute((const void*)router_recheck_logits<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)rl_bytes);
+    router_recheck_logits<uint16_t><<<a.E, kRecheckThreads, rl_bytes, s>>>((const uint16_t*)a.u, a.wg, a.off, a.E,
+                                                                            a.d, a.recheck_count, a.recheck_list, a.z64);
+  } else {
+    (void)hipFuncSetAttribute((const void*)router_recheck_logits<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)rl_bytes);
+    router_recheck_logits<float><<<a.E, kRecheckThreads, rl_bytes, s>>>((const float*)a.u, a.wg, a.off, a.E, a.d,
+                                                                         a.recheck_count, a.recheck_list, a.z64);
+  }
   if (a.gate == MOE_GATE_SOFTMAX)
     router_recheck_select<MOE_GATE_SOFTMAX><<<64, 256, 0, s>>>(a.z64, a.E, a.K, a.bias, a.renorm, a.recheck_count,
                                                                a.recheck_list, a.topk_idx, a.topk_w);

@@ -24,7 +24,7 @@
  *    stored as one SwiGLU block of inner dim fs (concatenating the inner dims is the same as summing).
  *  - Activations u and the output h have dtype act_dtype (F32 or BF16, bf16 = raw uint16 bits).
  *  - Expert weights have dtype w_dtype. Supported (act, w) pairs: (F32, F32), (BF16, BF16),
- *    (BF16, FP8_E4M3). bf16 and fp8 weights need d % 256 == 0 and f % 128 == 0.
+ *    (BF16, FP8_E4M3). bf16 and fp8 weights need d % 256 == 0 and f % 128 == 0; d <= 8192.
  *  - Expert outputs y (per routed row and shared) are BF16 for FP8_E4M3 weights (the combine payload of
  *    the E4M3 design) and F32 otherwise.
  *  - On a non-OK status, moe_last_error() returns a message for the calling thread.
@@ -98,13 +98,20 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
  *  bias     [E] fp32 selection bias, used only with MOE_GATE_SIGMOID_BIAS (NULL = zeros).
  *  topk_idx [T, K] int32 out: the selected routed experts of each token in ascending expert order.
  *           Keys are compared in fp32 and every token whose K-th and (K+1)-th keys are closer than
- *           1e-4 is decided again from fp64 logits, so the set is the exact top-K; ties go to the
- *           lower expert index.
+ *           2e-4 (softmax: logit units) or 4e-5 (sigmoid + bias) is decided again from fp64 logits, so
+ *           the set is the exact top-K; ties go to the lower expert index.
  *  topk_w   [T, K] fp32 out: gates, same order. Softmax: the probability over all E routed experts
  *           (renormalised over the K selected when cfg->renorm). Sigmoid: the affinity s, never s + b
  *           (renormalised when cfg->renorm). */
 moe_status moe_route(const moe_config* cfg, const moe_layer* layer, const void* u, const float* bias,
                      int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The router's fp32 logits alone (the first step of moe_route; for diagnostics and tests):
+ * z [T, E] fp32 out, z[t][i] = u_t . e_i + logit_offset[i], computed exactly as moe_route computes the
+ * keys it compares before the fp64 recheck (large bf16 batches: the centroids split into three bf16 parts
+ * on the matrix cores, fp32 accumulation; otherwise fp64 vector FMAs, rounded to fp32 once). */
+moe_status moe_router_logits(const moe_config* cfg, const moe_layer* layer, const void* u, float* z, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
 
 /* Dispatch: expert histogram, exclusive prefix sum and permutation into expert-contiguous rows.
  *  topk_idx [T, K] int32 in (as written by moe_route: distinct experts per token).
