@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--workload", default="v3_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens of the workload the oracle runs")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size kernel that profiler "
+                         "counters of HBM traffic are scaled against)")
     return ap.parse_args()
 
 
@@ -77,6 +80,20 @@ def roofline(work, ms, peak_mfma):
     ach = work["flops"] / t / 1e12
     return {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_mfma / 1e12, "unit": "TFLOP/s",
             "frac": round(ach / (peak_mfma / 1e12), 4), "traffic": None}
+
+
+def profiled_traffic(workload):
+    """HBM bytes per launch of the two grouped GEMM kernels from the committed counter profile of this
+    workload (profiles/traffic_<workload>.json), or None when the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, rec["kernel_source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec
 
 
 def cpu_model():
@@ -152,6 +169,14 @@ def main():
     from synth import configs
 
     w = configs.WORKLOADS[args.workload]
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t_setup = time.time()
     L = layers.device_layer(w)
     setup_s = time.time() - t_setup
@@ -208,6 +233,7 @@ def main():
                    "bias_update": w.gamma is not None},
         "roofline": dict(kernel="grouped_gemm_mfma gate/up+SwiGLU" if w.wdt != "f32" else "grouped_gemm_simt gate/up",
                          **roofline(gwork, stage["gateup"], peak)),
+        "algorithmic_bytes": {"gateup": int(gwork["bytes"]), "down": int(dwork["bytes"])},
         "grouped_gemm_tflops": round(gemm_tflops, 1),
         "grouped_gemm_mfma_frac": round(gemm_tflops * 1e12 / peak, 4),
         "down_roofline": roofline(dwork, stage["down"], peak),
@@ -215,6 +241,10 @@ def main():
         "touched_experts": touched,
         "setup_s": round(setup_s, 1),
     }
+    prof = profiled_traffic(w.name)
+    if prof is not None:
+        out["roofline"]["traffic"] = round(prof["gateup"]["traffic_bytes"])
+        out["down_roofline"]["traffic"] = round(prof["down"]["traffic_bytes"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
     print(json.dumps(out), flush=True)

@@ -1,0 +1,103 @@
+"""The C ABI without a GPU: every declared entry point is exported, and argument validation returns the
+documented status before anything is launched (these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fine_grained_mixture_gemm_amd as moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\*)\s+(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert "moe_forward" in names and len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        getattr(lib, n)
+
+
+def _cfg(**kw):
+    base = dict(T=64, d_model=256, n_routed=16, n_shared=1, top_k=4, inter_dim=128, gate=moe.MOE_GATE_SIGMOID_BIAS,
+                renorm=1, act_dtype=moe.MOE_BF16, w_dtype=moe.MOE_FP8_E4M3)
+    base.update(kw)
+    return moe.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=17, n_routed=32), moe.MOE_ERR_UNSUPPORTED),
+    (dict(top_k=20), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_routed=300, top_k=4), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(d_model=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(gate=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(renorm=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(act_dtype=moe.MOE_FP8_E4M3), moe.MOE_ERR_INVALID_ARG),
+    (dict(act_dtype=moe.MOE_F32, w_dtype=moe.MOE_BF16), moe.MOE_ERR_UNSUPPORTED),
+    (dict(d_model=384), moe.MOE_ERR_UNSUPPORTED),          # bf16 / fp8 experts need d % 256 == 0
+    (dict(inter_dim=100), moe.MOE_ERR_UNSUPPORTED),
+    (dict(d_model=8448), moe.MOE_ERR_UNSUPPORTED),         # fp64 recheck holds d <= 8192
+])
+def test_invalid_configs(kw, status):
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_workspace_size(_cfg(**kw))
+    assert e.value.status == status
+    assert moe.moe_last_error()
+
+
+def test_workspace_size_and_valid_configs():
+    assert moe.moe_workspace_size(_cfg()) > 0
+    assert moe.moe_workspace_size(_cfg(T=0)) > 0
+    assert moe.moe_workspace_size(_cfg(act_dtype=moe.MOE_F32, w_dtype=moe.MOE_F32, d_model=100, inter_dim=30)) > 0
+    big = moe.moe_workspace_size(_cfg(T=8192, d_model=7168, n_routed=256, top_k=8, inter_dim=2048))
+    assert 1e9 < big < 2e9
+
+
+def test_null_pointers_and_workspace_errors():
+    cfg = _cfg()
+    layer = moe.moe_layer()
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    lib.moe_route.argtypes = [ctypes.POINTER(moe.moe_config), ctypes.POINTER(moe.moe_layer)] + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]
+    # layer without w_gate
+    assert lib.moe_route(ctypes.byref(cfg), ctypes.byref(layer), 1, None, 1, 1, 1, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    layer.w_gate = 16
+    # u missing
+    assert lib.moe_route(ctypes.byref(cfg), ctypes.byref(layer), None, None, 16, 16, 16, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    # workspace too small or missing
+    assert lib.moe_route(ctypes.byref(cfg), ctypes.byref(layer), 16, None, 16, 16, 16, 1024, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(cfg), ctypes.byref(layer), 16, None, 16, 16, None, 1 << 30, None) == moe.MOE_ERR_WORKSPACE
+    # expert weights: fp8 needs scales
+    lib.moe_expert_ffn.argtypes = [ctypes.POINTER(moe.moe_config), ctypes.POINTER(moe.moe_layer)] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]
+    layer.w13, layer.w2 = 16, 16
+    assert lib.moe_expert_ffn(ctypes.byref(cfg), ctypes.byref(layer), 16, 16, 16, 16, 16, 16, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert "scale" in moe.moe_last_error()
+    # quantizers
+    lib.moe_quantize_weights.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.moe_quantize_weights(16, 1, 100, 128, 16, 16, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_weights(None, 1, 128, 128, 16, 16, None) == moe.MOE_ERR_INVALID_ARG
+    lib.moe_quantize_act.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.moe_quantize_act(16, moe.MOE_FP8_E4M3, 4, 128, 16, 16, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_act(16, moe.MOE_BF16, 4, 100, 16, 16, None) == moe.MOE_ERR_UNSUPPORTED
+    # timing marks need the full set of events
+    lib.moe_set_timing_events.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    assert lib.moe_set_timing_events(16, 3) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_set_timing_events(None, 0) == moe.MOE_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        moe.moe_quantize_act(torch.zeros(4, 128), moe.MOE_F32, torch.zeros(4, 128, dtype=torch.uint8), torch.zeros(4, 1))
