@@ -75,6 +75,10 @@ moe_status check_cfg(const moe_config* c) {
   if (c->w_dtype != MOE_F32 && (c->d_model % 256 != 0 || c->inter_dim % 128 != 0))
     return fail(MOE_ERR_UNSUPPORTED, "bf16/fp8 experts need d %% 256 == 0 and f %% 128 == 0 (d=%d f=%d)", c->d_model,
                 c->inter_dim);
+  // the E4M3 GEMM holds one weight block scale per 128-element K block in one lane of a wave
+  if (c->w_dtype == MOE_FP8_E4M3 && (long long)std::max(1, c->n_shared) * c->inter_dim > 8192)
+    return fail(MOE_ERR_UNSUPPORTED, "E4M3 experts need max(1, n_shared) * inter_dim <= 8192 (got %d * %d)",
+                c->n_shared, c->inter_dim);
   const long long rows = (long long)c->T * c->top_k;
   if (rows >= (1LL << 31) || (long long)c->n_shared * c->inter_dim >= (1LL << 30))
     return fail(MOE_ERR_UNSUPPORTED, "T*K or Ks*f too large");

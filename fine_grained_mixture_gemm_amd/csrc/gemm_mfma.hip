@@ -10,42 +10,47 @@
 // and added into an fp32 accumulator (promotion interval 128); the gate/up epilogue quantizes a
 // again per row per 128 columns.
 //
-// Tile: 256 weight rows x 128 tokens, K staged 128 bytes at a time (128 E4M3 or 64 bf16 elements).
-// The product is formed transposed (weights as the MFMA A operand, tokens as B) so that each lane's
-// accumulators belong to one token: the token's scale is one value per lane and the 1x128 requant
-// reduces over channels held by the same lane. Four waves (one per SIMD) each own 64 weight rows (for
-// gate/up: 32 gate channels and the same 32 up channels) against all 128 tokens.
-// Operands move global -> LDS by the LDS-DMA loads (no registers), into a ring of three stages: two
-// stages are in flight while the third is multiplied, which covers the HBM latency of the weight
-// stream. LDS rows are XOR-swizzled in 16-byte chunks (chunk c of row r sits at c ^ (r & 7)), so the
-// MFMA operand reads are free of bank conflicts.
+// Tile: 256 weight rows x 256 tokens, K streamed 128 bytes (128 E4M3 or 64 bf16 elements) per stage,
+// so one stage moves 64 KB for 8.4 M multiply-adds. The product is formed transposed (weights as the
+// MFMA A operand, tokens as B) so that each lane's accumulators belong to one token: the token's scale
+// is one value per lane and the 1x128 requant reduces over channels held by one lane group. Eight waves
+// (two per SIMD) each own 64 weight rows (gate/up: 32 gate channels and the same 32 up channels)
+// against 128 tokens; the two waves of a SIMD share weight rows and split the tokens.
+// Both operands move global -> LDS by the LDS-DMA loads, 8 lanes per 128-byte row so that every load
+// instruction touches whole cache lines (gathering 16 rows x 64 B per instruction, the MFMA operand
+// layout, runs the vector L1 at a third of that rate). The ring has two stages: one is multiplied while
+// the next one loads. LDS rows are XOR-swizzled in 16-byte chunks (chunk c of row r sits at c ^ (r & 7))
+// so that the MFMA operand reads are free of bank conflicts.
+// Each block walks its tiles as one continuous stream of stages (the first stage of the next tile
+// loads while the last stage of the current one is multiplied), and the epilogue stores straight from
+// registers. Waves whose 128 tokens all lie past the tile's last row skip the multiply.
 // The grid is persistent: blocks are split by XCD (block id mod 8) and each XCD walks one contiguous
 // range of the tile list, in which neighbouring tiles share an expert's weight tile in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
 
+#include <utility>
+
 namespace moe {
 
-constexpr int kBM = 128;        // tokens per tile
-constexpr int kBW = 256;        // weight rows per tile
-constexpr int kStageB = 128;    // K bytes per stage
-#ifndef MOE_GEMM_WM
-#define MOE_GEMM_WM 2
-#endif
-constexpr int kWM = MOE_GEMM_WM;          // waves along the tokens (each takes 128 / kWM tokens)
-constexpr int kThreads = 256 * kWM;       // 4 weight-row groups x kWM token groups
-constexpr int kTJ = 8 / kWM;              // 16-token MFMA tiles per wave
-constexpr int kG = kThreads / 8;          // LDS rows covered by one pass of the loader
-constexpr int kStages = 3;      // LDS ring depth
-constexpr int kAChunks = kBW * 8 / kThreads;   // 16-byte A chunks each thread moves per stage (8)
-constexpr int kBChunks = kBM * 8 / kThreads;   // 16-byte B chunks each thread moves per stage (4)
-constexpr int kSlotA = kBW * kStageB;          // 32 KB
-constexpr int kSlotB = kBM * kStageB;          // 16 KB
-constexpr int kSlotS = kSlotA + kSlotB;          // token scales [128] then the two weight scales
-constexpr int kSlot = kSlotS + kBM * 4 + 16;
-constexpr int kLdsBytes = kStages * kSlot;
-static_assert(kLdsBytes >= kBM * 512 + 4 * kBM * 4, "the epilogue reuses the ring");
+constexpr int kBM = 256;                         // tokens per tile
+constexpr int kBW = 256;                         // weight rows per tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStageB = 128;                     // K bytes per stage
+constexpr int kTJ = 8;                           // 16-token MFMA tiles per wave (128 tokens)
+constexpr int kChunks = kBW * 8 / kThreads;      // 16-byte chunks each thread moves per operand per stage
+constexpr int kSlotA = kBW * kStageB;            // 32 KB of weight rows
+constexpr int kSlotB = kBM * kStageB;            // 32 KB of token rows
+constexpr int kSX = kSlotA + kSlotB;             // one E4M3 scale per token
+constexpr int kWS = kSX + kBM * 4;               // the stage's two weight block scales
+constexpr int kSlot = kWS + 16;
+constexpr int kRed = 2 * kSlot;                  // epilogue exchange of row maxima [4][kBM] floats
+constexpr int kTab = kRed + 4 * kBM * 4;         // copies of the tile prefix and group offsets
+constexpr int kMaxGroups = 257;
+constexpr int kLdsBytes = kTab + 2 * kMaxGroups * 4;
+static_assert(kBW == kBM && kChunks == 4 && kLdsBytes <= 160 * 1024, "geometry");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -57,90 +62,134 @@ __device__ __forceinline__ void dma4(const void* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 4, 0, 0);
 }
 
-// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 s_waitcnt fields:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]; expcnt and lgkmcnt left at "no wait").
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+// Wait until this wave has no vector-memory operation in flight (its LDS-DMA copies have landed).
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
+
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations (lgkmcnt 0); the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// One K stage from an LDS slot. E4M3: each 16x16x128 product is a fresh partial sum that is scaled
-// and added into fp32; the products of token tile j+1 are issued before the additions of tile j so the
-// matrix core and the vector ALU work side by side.
+// Tile id -> (group, N tile, rows), from LDS copies of mt_prefix and offsets: routed experts ascending,
+// M index fastest within an expert, then the shared group.
+__device__ __forceinline__ TileInfo decode_tile_lds(int id, const int32_t* mtp, const int32_t* off, int E, int T,
+                                                    int nt_r) {
+  TileInfo ti;
+  const int routed_tiles = mtp[E] * nt_r;
+  if (id < routed_tiles) {
+    int lo = 0, hi = E;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (mtp[mid] * nt_r <= id) lo = mid;
+      else hi = mid - 1;
+    }
+    const int e = __builtin_amdgcn_readfirstlane(lo);
+    const int p0 = mtp[e];
+    const int mt = mtp[e + 1] - p0;
+    const int local = id - p0 * nt_r;
+    ti.group = e;
+    ti.n_tile = local / mt;
+    const int m_tile = local - ti.n_tile * mt;
+    const int o0 = off[e], n_e = off[e + 1] - o0;
+    ti.row0 = m_tile * kBM;
+    ti.nrows = min(kBM, n_e - ti.row0);
+    ti.rowbase = o0 + ti.row0;
+  } else {
+    const int mt = cdiv(T, kBM);
+    const int local = id - routed_tiles;
+    ti.group = E;
+    ti.n_tile = local / mt;
+    const int m_tile = local - ti.n_tile * mt;
+    ti.row0 = m_tile * kBM;
+    ti.nrows = min(kBM, T - ti.row0);
+    ti.rowbase = ti.row0;
+  }
+  ti.group = __builtin_amdgcn_readfirstlane(ti.group);
+  ti.n_tile = __builtin_amdgcn_readfirstlane(ti.n_tile);
+  ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
+  ti.nrows = __builtin_amdgcn_readfirstlane(ti.nrows);
+  ti.rowbase = __builtin_amdgcn_readfirstlane(ti.rowbase);
+  return ti;
+}
+
+// One K stage of one wave: its four 16-row weight tiles against its eight 16-token tiles. E4M3: every
+// 16x16x128 product is a fresh partial sum, scaled by (token scale x weight block scale) and added into
+// fp32 one MFMA after it is issued, so the matrix core and the vector ALU overlap.
 template <bool FP8, bool GATEUP>
 __device__ __forceinline__ void mma_stage(f32x4 (&acc)[4][kTJ], const uint8_t* __restrict__ slot, int wn, int tok0,
-                                          int lane) {
-  const int tr = lane & 15, g = lane >> 4;
+                                          int tr, int g) {
   const uint8_t* A = slot;
   const uint8_t* B = slot + kSlotA;
-  const float* SX = reinterpret_cast<const float*>(slot + kSlotS);
-  // this wave's four 16-row A tiles: gate/up LDS rows (i < 2 ? 0 : 128) + 32 wn + 16 (i & 1) (gate and
-  // up of the same channels); down LDS rows 64 wn + 16 i
+  auto rd = [&](const uint8_t* base, int row, i32x4& lo, i32x4& hi) {
+    lo = *reinterpret_cast<const i32x4*>(base + row * kStageB + ((g ^ (row & 7)) * 16));
+    hi = *reinterpret_cast<const i32x4*>(base + row * kStageB + (((4 + g) ^ (row & 7)) * 16));
+  };
+  // weight rows of tile i: gate/up -> gate rows 32 wn + 16 i (i < 2) and the matching up rows 128 + ...;
+  // down -> rows 64 wn + 16 i
   i32x4 a[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (GATEUP ? (i < 2 ? 0 : 128) + 32 * wn + 16 * (i & 1) : 64 * wn + 16 * i) + tr;
-    a[i][0] = *reinterpret_cast<const i32x4*>(A + row * kStageB + ((g ^ (row & 7)) * 16));
-    a[i][1] = *reinterpret_cast<const i32x4*>(A + row * kStageB + (((4 + g) ^ (row & 7)) * 16));
+    rd(A, row, a[i][0], a[i][1]);
   }
-  auto load_b = [&](int j, i32x4& b0, i32x4& b1) {
-    const int row = tok0 + 16 * j + tr;
-    b0 = *reinterpret_cast<const i32x4*>(B + row * kStageB + ((g ^ (row & 7)) * 16));
-    b1 = *reinterpret_cast<const i32x4*>(B + row * kStageB + (((4 + g) ^ (row & 7)) * 16));
-  };
+  i32x4 b[2][2];
+  rd(B, tok0 + tr, b[0][0], b[0][1]);
   if constexpr (FP8) {
-    const float s0 = SX[kBM], s1 = SX[kBM + 1];             // weight block scales of this stage
-    float swi[4];
+    const float* SX = reinterpret_cast<const float*>(slot + kSX);
+    const float* WSc = reinterpret_cast<const float*>(slot + kWS);
+    const float ws0 = WSc[0], ws1 = WSc[1];
+    float wsi[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) swi[i] = GATEUP ? (i < 2 ? s0 : s1) : (wn < 2 ? s0 : s1);
+    for (int i = 0; i < 4; ++i) wsi[i] = GATEUP ? (i < 2 ? ws0 : ws1) : (wn < 2 ? ws0 : ws1);
     i32x8 aa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       aa[i] = i32x8{a[i][0][0], a[i][0][1], a[i][0][2], a[i][0][3], a[i][1][0], a[i][1][1], a[i][1][2], a[i][1][3]};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 p[2][4];
-    float sx[2];
-    {
-      i32x4 b0, b1;
-      load_b(0, b0, b1);
-      const i32x8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[0][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa[i], bb, zero, 0, 0, 0, 127, 0, 127);
-      sx[0] = SX[tok0 + tr];
-    }
-#pragma unroll
-    for (int j = 0; j < kTJ; ++j) {
-      const int cur = j & 1, nxt = cur ^ 1;
-      if (j + 1 < kTJ) {
-        i32x4 b0, b1;
-        load_b(j + 1, b0, b1);
+    f32x4 p[2];
+    float cs[4];
+    float sxv[2];
+    sxv[0] = SX[tok0 + tr];
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      ([&] {
+        constexpr int j = J;
+        if constexpr (j + 1 < kTJ) rd(B, tok0 + 16 * (j + 1) + tr, b[(j + 1) & 1][0], b[(j + 1) & 1][1]);
+        const i32x4 b0 = b[j & 1][0], b1 = b[j & 1][1];
         const i32x8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          p[nxt][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa[i], bb, zero, 0, 0, 0, 127, 0, 127);
-        sx[nxt] = SX[tok0 + 16 * (j + 1) + tr];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sc = sx[cur] * swi[i];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, p[cur][i][r], acc[i][j][r]);
-      }
-    }
+        // token scales are read one 16-token tile ahead, like the token operand
+        if constexpr (j + 1 < kTJ) sxv[(j + 1) & 1] = SX[tok0 + 16 * (j + 1) + tr];
+        const float sx = sxv[j & 1];
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          ([&] {
+            constexpr int i = I;
+            p[i & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa[i], bb, zero, 0, 0, 0, 127, 0, 127);
+            // the product issued one MFMA earlier: tile (i - 1, j), or (3, j - 1) for i = 0
+            if constexpr (i > 0) acc[i - 1][j] += cs[i - 1] * p[(i - 1) & 1];
+            else if constexpr (j > 0) acc[3][j - 1] += cs[3] * p[1];
+            cs[i] = sx * wsi[i];
+          }(), ...);
+        }(std::make_integer_sequence<int, 4>{});
+      }(), ...);
+    }(std::make_integer_sequence<int, kTJ>{});
+    acc[3][kTJ - 1] += cs[3] * p[1];
   } else {
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      ([&] {
+        constexpr int j = J;
+        if constexpr (j + 1 < kTJ) rd(B, tok0 + 16 * (j + 1) + tr, b[(j + 1) & 1][0], b[(j + 1) & 1][1]);
 #pragma unroll
-    for (int j = 0; j < kTJ; ++j) {
-      i32x4 b0, b1;
-      load_b(j, b0, b1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i][0]),
-                                                            __builtin_bit_cast(bf16x8, b0), acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i][1]),
-                                                            __builtin_bit_cast(bf16x8, b1), acc[i][j], 0, 0, 0);
-      }
-    }
+        for (int i = 0; i < 4; ++i) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i][0]),
+                                                              __builtin_bit_cast(bf16x8, b[j & 1][0]), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i][1]),
+                                                              __builtin_bit_cast(bf16x8, b[j & 1][1]), acc[i][j], 0, 0, 0);
+        }
+      }(), ...);
+    }(std::make_integer_sequence<int, kTJ>{});
   }
 }
 
@@ -149,102 +198,154 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave & 3, wm = wave >> 2, tok0 = (128 / kWM) * wm;
-  const int esz = FP8 ? 1 : 2;
-  const int mt_routed = a.mt_prefix[a.E];
-  const int fr = a.f, fs = a.fs;
-  const int nt_r = GATEUP ? fr / 128 : a.d / kBW;
-  const int nt_s = GATEUP ? fs / 128 : a.d / kBW;
-  const int total = mt_routed * nt_r + (fs > 0 ? cdiv(a.T, kBM) * nt_s : 0);
+  const int wn = wave & 3, wm = wave >> 2, tok0 = 128 * wm;
+  const int tr = lane & 15, g = lane >> 4;
+  constexpr int esz = FP8 ? 1 : 2;
+  const int E = a.E;
+  const int nt_r = GATEUP ? a.f / 128 : a.d / kBW;
+  const int nt_s = GATEUP ? a.fs / 128 : a.d / kBW;
 
-  const int xcd = blockIdx.x & 7, slot_id = blockIdx.x >> 3, per = gridDim.x >> 3;
+  // the tile prefix and group offsets, copied once into LDS so that decoding a tile never waits on memory
+  int32_t* mtp = reinterpret_cast<int32_t*>(lds + kTab);
+  int32_t* goff = mtp + kMaxGroups;
+  for (int i = tid; i <= E; i += kThreads) {
+    mtp[i] = a.mt_prefix[i];
+    goff[i] = a.offsets[i];
+  }
+  barrier_lds();
+  const int mt_routed = __builtin_amdgcn_readfirstlane(mtp[E]);
+  const int total = mt_routed * nt_r + (a.fs > 0 ? cdiv(a.T, kBM) * nt_s : 0);
+
+  const int xcd = blockIdx.x & 7, per = gridDim.x >> 3;
   const int chunk = cdiv(total, 8);
   const int t_begin = xcd * chunk, t_end = min(total, t_begin + chunk);
+  int id_l = t_begin + (blockIdx.x >> 3);
+  if (id_l >= t_end) return;
+  auto decode = [&](int id) { return decode_tile_lds(id, mtp, goff, E, a.T, nt_r); };
 
-  for (int id = t_begin + slot_id; id < t_end; id += per) {
-    const TileInfo ti = decode_tile<kBM>(id, a, nt_r, mt_routed);
-    const bool shared = ti.group == a.E;
-    const int fg = shared ? fs : fr;                       // inner dim of this group
-    const int kelems = GATEUP ? a.d : fg;                  // reduction length
-    const int kbytes = kelems * esz;
-    const int nst = kbytes / kStageB;
-    const int kblk = kelems / 128;                         // 128-element scale blocks along K
-    const uint8_t* __restrict__ W;
-    const float* __restrict__ WS = nullptr;
+  // ---- loader geometry. Thread tid moves, per stage and operand, chunks id = 512 q + tid (q < 4): LDS
+  // row id / 8 = 64 q + lrow, LDS position id % 8, which holds global chunk (id % 8) ^ (row & 7).
+  const int lrow = tid >> 3;
+  const int lchunk = ((tid & 7) ^ (lrow & 7)) * 16;
+  // perm_src entries of the next tile's rows, loaded a tile early (always in bounds: every group's rows
+  // lie below T*K). Rows 64 q + lrow for the token chunks, row tid for the token scales (waves 0-3).
+  TileInfo tn = decode(id_l);
+  int rawn[kChunks + 1];
+  auto row_in_tile = [&](const TileInfo& t, int q) { return min(q < kChunks ? q * 64 + lrow : tid, t.nrows - 1); };
+  auto fetch_rows = [&](const TileInfo& t) {
+#pragma unroll
+    for (int q = 0; q <= kChunks; ++q) rawn[q] = a.perm_src[t.rowbase + row_in_tile(t, q)];
+  };
+  fetch_rows(tn);
+
+  TileInfo tl;
+  const uint8_t* Wl = nullptr;
+  const uint8_t* Xl = nullptr;
+  const float* XSl = nullptr;
+  const float* WSl = nullptr;
+  int nst_l = 0, kl = 0, kblk_l = 0, kbytes_l = 0, fg_l = 0;
+  bool live = true;
+  uint32_t boff[kChunks], sxoff = 0;
+  auto setup = [&]() {
+    tl = tn;
+    const bool shared = tl.group == E;
+    fg_l = shared ? a.fs : a.f;
+    const int kelems = GATEUP ? a.d : fg_l;
+    kbytes_l = kelems * esz;
+    kblk_l = kelems / 128;
+    nst_l = kbytes_l / kStageB;
+    const float* WS = nullptr;
     if (GATEUP) {
-      W = shared ? a.w_shared : a.w_routed + (size_t)ti.group * (2 * (size_t)fr) * a.d * esz;
-      if (FP8) WS = shared ? a.ws_shared : a.ws_routed + (size_t)ti.group * (2 * fr / 128) * (a.d / 128);
+      Wl = shared ? a.w_shared : a.w_routed + (size_t)tl.group * (2 * (size_t)a.f) * a.d * esz;
+      if (FP8) WS = shared ? a.ws_shared : a.ws_routed + (size_t)tl.group * (2 * a.f / 128) * (a.d / 128);
     } else {
-      W = shared ? a.w_shared : a.w_routed + (size_t)ti.group * (size_t)a.d * fr * esz;
-      if (FP8) WS = shared ? a.ws_shared : a.ws_routed + (size_t)ti.group * (a.d / 128) * (fr / 128);
+      Wl = shared ? a.w_shared : a.w_routed + (size_t)tl.group * (size_t)a.d * a.f * esz;
+      if (FP8) WS = shared ? a.ws_shared : a.ws_routed + (size_t)tl.group * (a.d / 128) * (a.f / 128);
     }
-    const uint8_t* __restrict__ X = shared ? a.x_shared : a.x_routed;
-    const float* __restrict__ XS = FP8 ? (shared ? a.xs_shared : a.xs_routed) : nullptr;
-    const int c0 = ti.n_tile * (GATEUP ? 128 : kBW);
+    Xl = shared ? a.x_shared : a.x_routed;
+    if (FP8) XSl = shared ? a.xs_shared : a.xs_routed;
+    const bool gather = GATEUP && !shared;
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) {
+      const int r = gather ? rawn[q] : tl.rowbase + row_in_tile(tl, q);
+      boff[q] = (uint32_t)r * kbytes_l + lchunk;
+    }
+    if (FP8) {
+      const int r = gather ? rawn[kChunks] : tl.rowbase + row_in_tile(tl, kChunks);
+      sxoff = (uint32_t)r * kblk_l;
+      // lane 0 of wave 4 copies the scale of block row c0 / 128 (gate, or the first 128 down rows),
+      // lane 1 that of (fg + c0) / 128 (up) or c0 / 128 + 1 (the next 128 down rows)
+      const int c0 = tl.n_tile * (GATEUP ? 128 : kBW);
+      const int brow = lane == 0 ? c0 / 128 : (GATEUP ? (fg_l + c0) / 128 : c0 / 128 + 1);
+      WSl = WS + (size_t)brow * kblk_l;
+    }
+    // the offsets are final before rawn is reloaded into the same registers
+    asm volatile("" ::"v"(boff[0]), "v"(boff[1]), "v"(boff[2]), "v"(boff[3]), "v"(sxoff) : "memory");
+    kl = 0;
+  };
+  setup();
+  if (id_l + per < t_end) {
+    tn = decode(id_l + per);
+    fetch_rows(tn);
+  }
 
-    // ---- loader geometry. Thread tid moves, per stage, A chunks id = q*256 + tid (q < 8) and B chunks
-    // id = q*256 + tid (q < 4): LDS row id / 8, LDS position p = id % 8, holding global chunk p ^ (row & 7).
-    const int lrow = tid >> 3;                             // row within a kG-row group
-    const int lchunk = ((tid & 7) ^ (lrow & 7)) * 16;      // global chunk of this thread's LDS position
-    // LDS A row r = kG q + lrow holds weight row c0 + lrow + wrow(q), wrow wave-uniform:
-    //   gate/up: rows < 128 are W1 rows c0 + r, rows >= 128 are W3 rows fg + c0 + r - 128;
-    //   down:    W2 rows c0 + r.
-    const uint8_t* __restrict__ Wl = W + (size_t)(c0 + lrow) * kbytes + lchunk;
-    auto wrow_q = [&](int q) -> int {
-      const int r0 = kG * q;
-      return (GATEUP && r0 >= 128) ? fg + r0 - 128 : r0;
-    };
-    auto src_row = [&](int r) -> int {
-      const int rr = min(r, ti.nrows - 1);
-      if (GATEUP) return shared ? ti.rowbase + rr : a.perm_src[ti.rowbase + rr];
-      return ti.rowbase + rr;
-    };
-    uint32_t boff[kBChunks];
-#pragma unroll
-    for (int q = 0; q < kBChunks; ++q) boff[q] = (uint32_t)src_row(q * kG + lrow) * kbytes + lchunk;
-    const uint32_t sxoff = (FP8 && wave < 2) ? (uint32_t)src_row(tid) * kblk : 0u;
-    // the tile's two weight block-scale rows: gate/up -> blocks c0/128 (gate) and (fg + c0)/128 (up);
-    // down -> blocks c0/128 (row groups 0, 1) and c0/128 + 1 (groups 2, 3). Lanes 0/1 of wave 2 copy them.
-    const float* wsrow = FP8 ? WS + (size_t)((lane == 0 ? c0 : (GATEUP ? fg + c0 : c0 + 128)) / 128) * kblk : nullptr;
-
-    auto issue = [&](int kb) {
-      uint8_t* slot = lds + (kb % kStages) * kSlot;
-      const uint8_t* Xk = X + (size_t)kb * kStageB;
-#pragma unroll
-      for (int q = 0; q < kAChunks; ++q)
-        dma16(Wl + ((size_t)wrow_q(q) * kbytes + (size_t)kb * kStageB), slot + (q * kThreads + wave * 64) * 16);
-#pragma unroll
-      for (int q = 0; q < kBChunks; ++q) dma16(Xk + boff[q], slot + kSlotA + (q * kThreads + wave * 64) * 16);
-      if (FP8 && wave < 2) dma4(XS + sxoff + kb, slot + kSlotS + wave * 256);
-      if (FP8 && wave == 2 && lane < 2) dma4(wsrow + kb, slot + kSlotS + kBM * 4);
-    };
-
-    f32x4 acc[4][kTJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < kTJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    issue(0);
-    if (nst > 1) issue(1);
-    for (int kb = 0; kb < nst; ++kb) {
-      // stage kb landed (stage kb+1 may still be in flight), then every wave is past stage kb-1
-      if (kb + 1 < nst) {
-        if (FP8 && wave < 3) wait_vm<kAChunks + kBChunks + 1>();
-        else wait_vm<kAChunks + kBChunks>();
+  // Issue the loader's next stage into ring slot `sl`. A block with no tile left re-reads stage 0 of
+  // its last tile, so the loop stays uniform; that data is never multiplied.
+  auto issue = [&](uint8_t* sl) {
+    if (kl == nst_l) {
+      id_l += per;
+      if (id_l < t_end) {
+        setup();
+        if (id_l + per < t_end) {
+          tn = decode(id_l + per);
+          fetch_rows(tn);
+        }
       } else {
-        wait_vm<0>();
+        live = false;
       }
-      __builtin_amdgcn_s_barrier();
-      if (kb + 2 < nst) issue(kb + 2);
-      mma_stage<FP8, GATEUP>(acc, lds + (kb % kStages) * kSlot, wn, tok0, lane);
     }
-    __builtin_amdgcn_s_barrier();   // every wave is done with the ring before the epilogue reuses it
+    const int kk = live ? kl : 0;
+    ++kl;
+    // weight rows: LDS row 64 q + lrow is W1 row c0 + 64 q + lrow (q < 2) or W3 row fg + c0 + 64 q - 128 +
+    // lrow (gate/up, c0 = 128 n_tile); W2 row c0 + 64 q + lrow (down, c0 = 256 n_tile)
+    const int c0 = tl.n_tile * (GATEUP ? 128 : kBW);
+    const uint8_t* Wk = Wl + (size_t)kk * kStageB + lchunk;
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) {
+      const int wrow = (GATEUP && q >= 2) ? fg_l + c0 + 64 * q - 128 : c0 + 64 * q;
+      dma16(Wk + (size_t)(wrow + lrow) * kbytes_l, sl + (q * kThreads + wave * 64) * 16);
+    }
+    const uint8_t* Xk = Xl + (size_t)kk * kStageB;
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) dma16(Xk + boff[q], sl + kSlotA + (q * kThreads + wave * 64) * 16);
+    if (FP8 && wave < 4) dma4(XSl + sxoff + kk, sl + kSX + wave * 256);
+    if (FP8 && wave == 4 && lane < 2) dma4(WSl + kk, sl + kWS);
+  };
 
-    // ---- epilogue. Lane holds, for token tok0 + 16j + (lane & 15), weight-row channels 4 (lane >> 4) + r
-    // of each 16-row tile i.
-    const int tr = lane & 15, g4 = 4 * (lane >> 4);
+  // ---- compute: the tile being multiplied
+  TileInfo tc = tl;
+  int nst_c = nst_l, kb = 0, id_c = id_l;
+  f32x4 acc[4][kTJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < kTJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(lds);
+  for (int gs = 0;; ++gs) {
+    uint8_t* cur = lds + (gs & 1) * kSlot;
+    wait_vm0();       // this wave's copies of stage gs have landed
+    barrier_lds();    // ... and every wave's; every wave is done with the other slot
+    issue(lds + ((gs + 1) & 1) * kSlot);
+    if (tok0 < tc.nrows) mma_stage<FP8, GATEUP>(acc, cur, wn, tok0, tr, g);
+    if (++kb < nst_c) continue;
+
+    // ---- epilogue of tile tc. Lane holds, for token tok0 + 16 j + tr, channels 4 g + r of each 16-row
+    // weight tile i (gate/up: gate channels 32 wn + 16 i for i < 2, their up channels for i >= 2).
+    const bool shared = tc.group == E;
+    const int fg = shared ? a.fs : a.f;
     if constexpr (GATEUP) {
+      const int c0 = tc.n_tile * 128;
       float av[2][kTJ][4];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -252,11 +353,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
         for (int j = 0; j < kTJ; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) av[i][j][r] = silu(acc[i][j][r]) * acc[i + 2][j][r];
-      const size_t out_stride = (size_t)fg * esz;           // bytes per output row
-      uint8_t* OUT = (shared ? a.out_shared : a.out_routed) + (size_t)ti.rowbase * out_stride + (size_t)c0 * esz;
+      const size_t out_stride = (size_t)fg * esz;
+      uint8_t* OUT = (shared ? a.out_shared : a.out_routed) + (size_t)tc.rowbase * out_stride +
+                     (size_t)(c0 + 32 * wn + 4 * g) * esz;
       if constexpr (FP8) {
-        float* red = reinterpret_cast<float*>(lds + kBM * 128);   // [4 weight-row groups][128 tokens]
-        float inv[kTJ];
+        // 1x128 requant of a: a token's 128 channels of this tile are spread over the four wn waves
+        float* red = reinterpret_cast<float*>(lds + kRed);
 #pragma unroll
         for (int j = 0; j < kTJ; ++j) {
           float m = 0.f;
@@ -268,93 +370,76 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
           m = fmaxf(m, __shfl_xor(m, 32, 64));
           if (lane < 16) red[wn * kBM + tok0 + 16 * j + tr] = m;
         }
-        __syncthreads();
-        float* OS = (shared ? a.out_scale_shared : a.out_scale_routed);
+        barrier_lds();
+        float* OS = shared ? a.out_scale_shared : a.out_scale_routed;
 #pragma unroll
         for (int j = 0; j < kTJ; ++j) {
           const int tok = tok0 + 16 * j + tr;
           const float m = fmaxf(fmaxf(red[tok], red[kBM + tok]), fmaxf(red[2 * kBM + tok], red[3 * kBM + tok]));
-          float s;
-          e4m3_scales(m, s, inv[j]);
-          if (wn == 0 && lane < 16 && tok < ti.nrows) OS[(size_t)(ti.rowbase + tok) * (fg / 128) + ti.n_tile] = s;
-        }
+          float s, inv;
+          e4m3_scales(m, s, inv);
+          if (tok < tc.nrows) {
+            if (wn == 0 && g == 0) OS[(size_t)(tc.rowbase + tok) * (fg / 128) + tc.n_tile] = s;
 #pragma unroll
-        for (int j = 0; j < kTJ; ++j)
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int tok = tok0 + 16 * j + tr, ch = 32 * wn + 16 * i + g4;
-            const uint32_t qv = f32x4_to_e4m3x4(av[i][j][0] * inv[j], av[i][j][1] * inv[j], av[i][j][2] * inv[j],
-                                                av[i][j][3] * inv[j]);
-            *reinterpret_cast<uint32_t*>(lds + tok * 128 + ch) = qv;
+            for (int i = 0; i < 2; ++i)
+              *reinterpret_cast<uint32_t*>(OUT + (size_t)tok * out_stride + 16 * i) =
+                  f32x4_to_e4m3x4(av[i][j][0] * inv, av[i][j][1] * inv, av[i][j][2] * inv, av[i][j][3] * inv);
           }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < kBM * 8 / kThreads; ++q) {
-          const int id16 = q * kThreads + tid, row = id16 >> 3, c = id16 & 7;
-          if (row < ti.nrows)
-            *reinterpret_cast<uint4*>(OUT + (size_t)row * out_stride + c * 16) =
-                *reinterpret_cast<const uint4*>(lds + row * 128 + c * 16);
         }
+        // `red` is written again only by the next epilogue, after at least one more barrier
       } else {
 #pragma unroll
-        for (int j = 0; j < kTJ; ++j)
+        for (int j = 0; j < kTJ; ++j) {
+          const int tok = tok0 + 16 * j + tr;
+          if (tok < tc.nrows) {
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int tok = tok0 + 16 * j + tr, ch = 32 * wn + 16 * i + g4;
-            uint2 v;
-            v.x = uint32_t(f32_to_bf16(av[i][j][0])) | (uint32_t(f32_to_bf16(av[i][j][1])) << 16);
-            v.y = uint32_t(f32_to_bf16(av[i][j][2])) | (uint32_t(f32_to_bf16(av[i][j][3])) << 16);
-            *reinterpret_cast<uint2*>(lds + tok * 256 + ch * 2) = v;
-          }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < kBM * 16 / kThreads; ++q) {
-          const int id16 = q * kThreads + tid, row = id16 >> 4, c = id16 & 15;
-          if (row < ti.nrows)
-            *reinterpret_cast<uint4*>(OUT + (size_t)row * out_stride + c * 16) =
-                *reinterpret_cast<const uint4*>(lds + row * 256 + c * 16);
-        }
-      }
-    } else if constexpr (!FP8) {
-      // y in fp32: each lane stores its 4 consecutive channels of one token (16 bytes)
-      const size_t out_stride = (size_t)a.d * 4;
-      uint8_t* OUT = (shared ? a.out_shared : a.out_routed) + (size_t)ti.rowbase * out_stride + (size_t)c0 * 4;
-#pragma unroll
-      for (int j = 0; j < kTJ; ++j) {
-        const int tok = tok0 + 16 * j + tr;
-        if (tok < ti.nrows) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ch = 64 * wn + 16 * i + g4;
-            *reinterpret_cast<f32x4*>(OUT + (size_t)tok * out_stride + ch * 4) = acc[i][j];
+            for (int i = 0; i < 2; ++i) {
+              uint2 v;
+              v.x = uint32_t(f32_to_bf16(av[i][j][0])) | (uint32_t(f32_to_bf16(av[i][j][1])) << 16);
+              v.y = uint32_t(f32_to_bf16(av[i][j][2])) | (uint32_t(f32_to_bf16(av[i][j][3])) << 16);
+              *reinterpret_cast<uint2*>(OUT + (size_t)tok * out_stride + 16 * i * esz) = v;
+            }
           }
         }
       }
     } else {
-      // y tile in bf16 (the combine payload of the E4M3 path): 128 tokens x 256 channels through LDS
-      const size_t out_stride = (size_t)a.d * 2;
-      uint8_t* OUT = (shared ? a.out_shared : a.out_routed) + (size_t)ti.rowbase * out_stride + (size_t)c0 * 2;
+      const int c0 = tc.n_tile * kBW;
+      constexpr int ysz = FP8 ? 2 : 4;   // y in bf16 (the combine payload of the E4M3 path) or fp32
+      const size_t out_stride = (size_t)a.d * ysz;
+      uint8_t* OUT = (shared ? a.out_shared : a.out_routed) + (size_t)tc.rowbase * out_stride +
+                     (size_t)(c0 + 64 * wn + 4 * g) * ysz;
 #pragma unroll
-      for (int j = 0; j < kTJ; ++j)
+      for (int j = 0; j < kTJ; ++j) {
+        const int tok = tok0 + 16 * j + tr;
+        if (tok < tc.nrows) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = tok0 + 16 * j + tr, ch = 64 * wn + 16 * i + g4;
-          uint2 v;
-          v.x = uint32_t(f32_to_bf16(acc[i][j][0])) | (uint32_t(f32_to_bf16(acc[i][j][1])) << 16);
-          v.y = uint32_t(f32_to_bf16(acc[i][j][2])) | (uint32_t(f32_to_bf16(acc[i][j][3])) << 16);
-          *reinterpret_cast<uint2*>(lds + tok * 512 + ch * 2) = v;
+          for (int i = 0; i < 4; ++i) {
+            uint8_t* o = OUT + (size_t)tok * out_stride + 16 * i * ysz;
+            if constexpr (FP8) {
+              uint2 v;
+              v.x = uint32_t(f32_to_bf16(acc[i][j][0])) | (uint32_t(f32_to_bf16(acc[i][j][1])) << 16);
+              v.y = uint32_t(f32_to_bf16(acc[i][j][2])) | (uint32_t(f32_to_bf16(acc[i][j][3])) << 16);
+              *reinterpret_cast<uint2*>(o) = v;
+            } else {
+              *reinterpret_cast<f32x4*>(o) = acc[i][j];
+            }
+          }
         }
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < kBM * 32 / kThreads; ++q) {
-        const int id16 = q * kThreads + tid, row = id16 >> 5, c = id16 & 31;
-        if (row < ti.nrows)
-          *reinterpret_cast<uint4*>(OUT + (size_t)row * out_stride + c * 16) =
-              *reinterpret_cast<const uint4*>(lds + row * 512 + c * 16);
       }
     }
-    __syncthreads();   // epilogue LDS reads finish before the next tile's first DMA
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kTJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    id_c += per;
+    if (id_c >= t_end) break;
+    // the loader moved to this tile while the last stage of the previous one was multiplied
+    tc = tl;
+    nst_c = nst_l;
+    kb = 0;
   }
+  wait_vm0();
 }
 
 int gemm_mfma_bm() { return kBM; }
