@@ -93,7 +93,7 @@ moe_status check_cfg(const moe_config* c) {
 
 struct Layout {
   size_t z, z64, wg_split, recheck_count, recheck_list;
-  size_t chunk_counts, chunk_base, mt_prefix;
+  size_t chunk_counts, chunk_base, mt_prefix, xsched;
   size_t uq, us, a_r, a_s, as_r, as_s;
   size_t f_idx, f_w, f_counts, f_offsets, f_perm, f_rowof, f_yr, f_ys;
   size_t total;
@@ -121,6 +121,7 @@ Layout layout(const moe_config* c) {
   L.chunk_counts = take(nch * E * 4);
   L.chunk_base = take(nch * E * 4);
   L.mt_prefix = take((E + 1) * 4);
+  L.xsched = take(2 * 9 * 4 + 2 * 8 * 4);
   L.uq = take(fp8 ? T * d : 0);
   L.us = take(fp8 ? T * (d / 128) * 4 : 0);
   L.a_r = take(rows * f * esz_a);
@@ -238,8 +239,16 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   const bool mfma = use_mfma_gemm(c);
   const int bm = mfma ? gemm_mfma_bm() : gemm_simt_bm();
   int32_t* mt_prefix = reinterpret_cast<int32_t*>(base + L.mt_prefix);
-  MOE_TRY(hip_status(launch_schedule(offsets, c->n_routed, bm, mt_prefix, s), "schedule launch"));
+  int32_t* xrange = reinterpret_cast<int32_t*>(base + L.xsched);
+  int32_t* xcount = xrange + 2 * 9;
   const int fs = c->n_shared * c->inter_dim;
+  if (mfma) {
+    const int nt_r[2] = {c->inter_dim / 128, c->d_model / 256}, nt_s[2] = {fs / 128, fs > 0 ? c->d_model / 256 : 0};
+    MOE_TRY(hip_status(launch_schedule_mfma(offsets, c->n_routed, c->T, bm, nt_r, nt_s, mt_prefix, xrange, xcount, s),
+                       "schedule launch"));
+  } else {
+    MOE_TRY(hip_status(launch_schedule(offsets, c->n_routed, bm, mt_prefix, s), "schedule launch"));
+  }
   GemmArgs g{};
   g.E = c->n_routed;
   g.T = c->T;
@@ -249,6 +258,8 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   g.offsets = offsets;
   g.perm_src = perm;
   g.mt_prefix = mt_prefix;
+  g.xrange = xrange;
+  g.xcount = xcount;
   const uint8_t* xin = static_cast<const uint8_t*>(u);
   const float* xs = nullptr;
   if (fp8) {
@@ -295,6 +306,8 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   g.out_shared = static_cast<uint8_t*>(y_s);
   g.out_scale_routed = nullptr;
   g.out_scale_shared = nullptr;
+  g.xrange = xrange + 9;
+  g.xcount = xcount + 8;
   if (mfma) {
     const int grid = device_cus() / 8 * 8;
     MOE_TRY(hip_status(launch_gemm_mfma(g, fp8, false, grid, s), "down GEMM launch"));

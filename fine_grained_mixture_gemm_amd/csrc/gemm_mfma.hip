@@ -49,7 +49,8 @@ constexpr int kSlot = kWS + 16;
 constexpr int kRed = 2 * kSlot;                  // epilogue exchange of row maxima [4][kBM] floats
 constexpr int kTab = kRed + 4 * kBM * 4;         // copies of the tile prefix and group offsets
 constexpr int kMaxGroups = 257;
-constexpr int kLdsBytes = kTab + 2 * kMaxGroups * 4;
+constexpr int kIds = kTab + 2 * kMaxGroups * 4 + 8;   // ring of the block's next tile ids
+constexpr int kLdsBytes = kIds + 16;
 static_assert(kBW == kBM && kChunks == 4 && kLdsBytes <= 160 * 1024, "geometry");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -203,7 +204,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
   constexpr int esz = FP8 ? 1 : 2;
   const int E = a.E;
   const int nt_r = GATEUP ? a.f / 128 : a.d / kBW;
-  const int nt_s = GATEUP ? a.fs / 128 : a.d / kBW;
 
   // the tile prefix and group offsets, copied once into LDS so that decoding a tile never waits on memory
   int32_t* mtp = reinterpret_cast<int32_t*>(lds + kTab);
@@ -212,15 +212,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
     mtp[i] = a.mt_prefix[i];
     goff[i] = a.offsets[i];
   }
+  // This XCD's range of the tile list; its blocks take tiles in order from the XCD's counter. Tile k of
+  // the block has id ids[k % 4]: the ring holds the next three, and one more request is in flight.
+  const int xcd = blockIdx.x & 7;
+  const int t_begin = a.xrange[xcd], t_end = a.xrange[xcd + 1];
+  int32_t* ids = reinterpret_cast<int32_t*>(lds + kIds);
+  int pending = 0;
+  if (tid == 0) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) ids[k] = t_begin + atomicAdd(a.xcount + xcd, 1);
+    pending = t_begin + atomicAdd(a.xcount + xcd, 1);
+  }
   barrier_lds();
-  const int mt_routed = __builtin_amdgcn_readfirstlane(mtp[E]);
-  const int total = mt_routed * nt_r + (a.fs > 0 ? cdiv(a.T, kBM) * nt_s : 0);
-
-  const int xcd = blockIdx.x & 7, per = gridDim.x >> 3;
-  const int chunk = cdiv(total, 8);
-  const int t_begin = xcd * chunk, t_end = min(total, t_begin + chunk);
-  int id_l = t_begin + (blockIdx.x >> 3);
+  int id_l = __builtin_amdgcn_readfirstlane(ids[0]);
   if (id_l >= t_end) return;
+  int ktile = 0;                           // tiles the loader has started, minus one
+  auto next_id = [&](int k) { return __builtin_amdgcn_readfirstlane(ids[k & 3]); };
   auto decode = [&](int id) { return decode_tile_lds(id, mtp, goff, E, a.T, nt_r); };
 
   // ---- loader geometry. Thread tid moves, per stage and operand, chunks id = 512 q + tid (q < 4): LDS
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
   const uint8_t* Xl = nullptr;
   const float* XSl = nullptr;
   const float* WSl = nullptr;
-  int nst_l = 0, kl = 0, kblk_l = 0, kbytes_l = 0, fg_l = 0;
+  int nst_l = 0, kl = 0, kblk_l = 0, kbytes_l = 0, fg_l = 0, started = 1;
   bool live = true;
   uint32_t boff[kChunks], sxoff = 0;
   auto setup = [&]() {
@@ -284,21 +291,30 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
     kl = 0;
   };
   setup();
-  if (id_l + per < t_end) {
-    tn = decode(id_l + per);
+  int id_n = next_id(1);
+  if (id_n < t_end) {
+    tn = decode(id_n);
     fetch_rows(tn);
   }
 
   // Issue the loader's next stage into ring slot `sl`. A block with no tile left re-reads stage 0 of
   // its last tile, so the loop stays uniform; that data is never multiplied.
   auto issue = [&](uint8_t* sl) {
-    if (kl == nst_l) {
-      id_l += per;
+    if (kl == nst_l && live) {
+      ++ktile;
+      id_l = next_id(ktile);
       if (id_l < t_end) {
         setup();
-        if (id_l + per < t_end) {
-          tn = decode(id_l + per);
+        ++started;
+        id_n = next_id(ktile + 1);
+        if (id_n < t_end) {
+          tn = decode(id_n);
           fetch_rows(tn);
+        }
+        // the id of tile ktile + 2 arrived a tile ago; request the one after it
+        if (tid == 0) {
+          ids[(ktile + 2) & 3] = pending;
+          pending = t_begin + atomicAdd(a.xcount + xcd, 1);
         }
       } else {
         live = false;
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
 
   // ---- compute: the tile being multiplied
   TileInfo tc = tl;
-  int nst_c = nst_l, kb = 0, id_c = id_l;
+  int nst_c = nst_l, kb = 0, done = 0;
   f32x4 acc[4][kTJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -432,8 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < kTJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    id_c += per;
-    if (id_c >= t_end) break;
+    if (++done == started && !live) break;
     // the loader moved to this tile while the last stage of the previous one was multiplied
     tc = tl;
     nst_c = nst_l;

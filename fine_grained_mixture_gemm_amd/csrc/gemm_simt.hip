@@ -31,6 +31,88 @@ hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_pr
   return hipGetLastError();
 }
 
+// Schedule of the matrix-core grouped GEMMs. The tile list (routed experts ascending, M index fastest
+// within an N column, then the shared group) is cut into eight contiguous ranges of equal estimated
+// cost, one per XCD; a tile costs 10 when more than half of its bm rows are valid (both token halves
+// of the block multiply) and 7 otherwise (one half multiplies; streaming its weights still takes most
+// of the time). Within a range the blocks of that XCD take tiles in order from a counter.
+__global__ __launch_bounds__(256) void ffn_schedule_mfma(const int32_t* __restrict__ offsets, int E, int T, int bm,
+                                                         int ntr0, int nts0, int ntr1, int nts1,
+                                                         int32_t* __restrict__ mt_prefix, int32_t* __restrict__ xrange,
+                                                         int32_t* __restrict__ xcount) {
+  __shared__ int32_t s_mt[257], s_cost[257];
+  const int t = threadIdx.x;
+  auto column_cost = [&](int n, int& mt) {     // M tiles of a group with n rows and the cost of one N column
+    mt = cdiv(n, bm);
+    int c = 0;
+    for (int m = 0; m < mt; ++m) c += min(bm, n - m * bm) > bm / 2 ? 10 : 7;
+    return c;
+  };
+  for (int g = t; g <= E; g += 256) {
+    int mt;
+    const int n = g < E ? offsets[g + 1] - offsets[g] : T;
+    s_cost[g] = column_cost(n, mt);
+    s_mt[g] = mt;
+  }
+  if (t < 16) xcount[t] = 0;
+  __syncthreads();
+  if (t == 0) {
+    int m = 0;
+    for (int g = 0; g < E; ++g) {
+      mt_prefix[g] = m;
+      m += s_mt[g];
+    }
+    mt_prefix[E] = m;
+  }
+  if (t < 2) {
+    const int ntr = t == 0 ? ntr0 : ntr1, nts = t == 0 ? nts0 : nts1;
+    long long total = 0;
+    int tiles = 0;
+    for (int g = 0; g <= E; ++g) {
+      const int nt = g < E ? ntr : nts;
+      total += (long long)nt * s_cost[g];
+      tiles += nt * s_mt[g];
+    }
+    int32_t* r = xrange + 9 * t;
+    r[0] = 0;
+    r[8] = tiles;
+    // boundary x: the first tile whose preceding cost reaches x * total / 8. Within a group every N column
+    // costs s_cost[g]; the boundary's column follows by division and its M tile by a scan of one column.
+    int x = 1, id = 0;
+    long long before = 0;
+    for (int g = 0; g <= E && x < 8; ++g) {
+      const int nt = g < E ? ntr : nts, mt = s_mt[g], S = s_cost[g];
+      const int n = g < E ? offsets[g + 1] - offsets[g] : T;
+      const long long gend = before + (long long)nt * S;
+      while (x < 8 && total * x / 8 <= gend) {
+        const long long off = total * x / 8 - before;
+        if (off <= 0 || S == 0) {
+          r[x++] = id;
+          continue;
+        }
+        const int c0 = (int)(off / S);
+        const long long rem = off - (long long)c0 * S;
+        int mi = 0;
+        long long cum = 0;
+        while (mi < mt && cum < rem) {
+          cum += min(bm, n - mi * bm) > bm / 2 ? 10 : 7;
+          ++mi;
+        }
+        r[x++] = id + c0 * mt + mi;
+      }
+      before = gend;
+      id += nt * mt;
+    }
+    while (x < 8) r[x++] = tiles;
+  }
+}
+
+hipError_t launch_schedule_mfma(const int32_t* offsets, int E, int T, int bm, const int (&nt_r)[2], const int (&nt_s)[2],
+                                int32_t* mt_prefix, int32_t* xrange, int32_t* xcount, hipStream_t s) {
+  ffn_schedule_mfma<<<1, 256, 0, s>>>(offsets, E, T, bm, nt_r[0], nt_s[0], nt_r[1], nt_s[1], mt_prefix, xrange, xcount);
+  return hipGetLastError();
+}
+
 constexpr int kSBM = 64, kSBK = 16;
 
 template <bool GATEUP>

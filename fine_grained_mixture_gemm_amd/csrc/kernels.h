@@ -40,6 +40,8 @@ struct GemmArgs {
   const int32_t* offsets;
   const int32_t* perm_src;
   const int32_t* mt_prefix;   // [E+1] prefix of M tiles per routed expert
+  const int32_t* xrange;      // matrix-core path: [9] tile-id range of each XCD (cost-balanced)
+  int32_t* xcount;            // matrix-core path: [8] per-XCD tile counters, zero at launch
   const uint8_t* w_routed;    // w13 or w2 of all routed experts
   const uint8_t* w_shared;
   const float* ws_routed;     // fp8 block scales
@@ -62,6 +64,10 @@ int dispatch_chunks(int T);
 hipError_t launch_quant_act(const void* x, bool x_bf16, int rows, int cols, uint8_t* q, float* scales, hipStream_t s);
 hipError_t launch_quant_weight(const float* w, int batch, int rows, int cols, uint8_t* q, float* scales, hipStream_t s);
 hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_prefix, hipStream_t s);
+// M-tile prefix plus, for the gate/up (k = 0) and down (k = 1) launches of the matrix-core GEMM, the
+// cost-balanced XCD ranges xrange[k][9] and zeroed tile counters xcount[k][8].
+hipError_t launch_schedule_mfma(const int32_t* offsets, int E, int T, int bm, const int (&nt_r)[2], const int (&nt_s)[2],
+                                int32_t* mt_prefix, int32_t* xrange, int32_t* xcount, hipStream_t s);
 int gemm_mfma_bm();
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s);
 int gemm_simt_bm();
