@@ -92,7 +92,7 @@ moe_status check_cfg(const moe_config* c) {
 }
 
 struct Layout {
-  size_t z, z64, wg_split, recheck_count, recheck_list;
+  size_t z, z64, wg_split, zpart, recheck_count, recheck_list;
   size_t chunk_counts, chunk_base, mt_prefix, xsched;
   size_t uq, us, a_r, a_s, as_r, as_s;
   size_t f_idx, f_w, f_counts, f_offsets, f_perm, f_rowof, f_yr, f_ys;
@@ -115,6 +115,9 @@ Layout layout(const moe_config* c) {
   L.z = take(T * E * 4);
   L.z64 = take(T * E * 8);
   L.wg_split = take(use_mfma_router(c) ? 3 * E * d * 2 : 0);
+  int klen = 0;
+  const int ksplit = use_mfma_router(c) ? 1 : router_ksplit((int)T, (int)E, (int)d, klen);
+  L.zpart = take(ksplit > 1 ? (size_t)ksplit * T * E * 8 : 0);
   L.recheck_count = take(16);
   L.recheck_list = take(T * 4);
   const size_t nch = dispatch_chunks(c->T);
@@ -198,6 +201,8 @@ RouteArgs route_args(const moe_config* c, const moe_layer* l, const void* u, con
   a.z = reinterpret_cast<float*>(base + L.z);
   a.z64 = reinterpret_cast<double*>(base + L.z64);
   a.wg_split = reinterpret_cast<uint16_t*>(base + L.wg_split);
+  a.ksplit = a.use_mfma ? 1 : router_ksplit(a.T, a.E, a.d, a.klen);
+  a.zpart = reinterpret_cast<double*>(base + L.zpart);
   a.recheck_count = reinterpret_cast<int*>(base + L.recheck_count);
   a.recheck_list = reinterpret_cast<int*>(base + L.recheck_list);
   a.topk_idx = idx;

@@ -76,9 +76,11 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 // Tile id -> (group, N tile, rows), from LDS copies of mt_prefix and offsets: routed experts ascending,
-// M index fastest within an expert, then the shared group.
+// N index fastest within an expert (the N tiles of one M tile share its token rows and run for equally
+// many stages, so blocks that take them together stay in step and read those rows from L2), then the
+// shared group in the same order.
 __device__ __forceinline__ TileInfo decode_tile_lds(int id, const int32_t* mtp, const int32_t* off, int E, int T,
-                                                    int nt_r) {
+                                                    int nt_r, int nt_s) {
   TileInfo ti;
   const int routed_tiles = mtp[E] * nt_r;
   if (id < routed_tiles) {
@@ -89,22 +91,19 @@ __device__ __forceinline__ TileInfo decode_tile_lds(int id, const int32_t* mtp, 
       else hi = mid - 1;
     }
     const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int p0 = mtp[e];
-    const int mt = mtp[e + 1] - p0;
-    const int local = id - p0 * nt_r;
+    const int local = id - mtp[e] * nt_r;
     ti.group = e;
-    ti.n_tile = local / mt;
-    const int m_tile = local - ti.n_tile * mt;
+    const int m_tile = local / nt_r;
+    ti.n_tile = local - m_tile * nt_r;
     const int o0 = off[e], n_e = off[e + 1] - o0;
     ti.row0 = m_tile * kBM;
     ti.nrows = min(kBM, n_e - ti.row0);
     ti.rowbase = o0 + ti.row0;
   } else {
-    const int mt = cdiv(T, kBM);
     const int local = id - routed_tiles;
     ti.group = E;
-    ti.n_tile = local / mt;
-    const int m_tile = local - ti.n_tile * mt;
+    const int m_tile = local / nt_s;
+    ti.n_tile = local - m_tile * nt_s;
     ti.row0 = m_tile * kBM;
     ti.nrows = min(kBM, T - ti.row0);
     ti.rowbase = ti.row0;
@@ -228,7 +227,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
   if (id_l >= t_end) return;
   int ktile = 0;                           // tiles the loader has started, minus one
   auto next_id = [&](int k) { return __builtin_amdgcn_readfirstlane(ids[k & 3]); };
-  auto decode = [&](int id) { return decode_tile_lds(id, mtp, goff, E, a.T, nt_r); };
+  const int nt_s = max(1, GATEUP ? a.fs / 128 : a.d / kBW);
+  auto decode = [&](int id) { return decode_tile_lds(id, mtp, goff, E, a.T, nt_r, nt_s); };
 
   // ---- loader geometry. Thread tid moves, per stage and operand, chunks id = 512 q + tid (q < 4): LDS
   // row id / 8 = 64 q + lrow, LDS position id % 8, which holds global chunk (id % 8) ^ (row & 7).

@@ -31,85 +31,91 @@ hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_pr
   return hipGetLastError();
 }
 
-// Schedule of the matrix-core grouped GEMMs. The tile list (routed experts ascending, M index fastest
-// within an N column, then the shared group) is cut into eight contiguous ranges of equal estimated
+// Schedule of the matrix-core grouped GEMMs. The tile list (routed experts ascending, N index fastest
+// within an M tile, then the shared group) is cut into eight contiguous ranges of equal estimated
 // cost, one per XCD; a tile costs 10 when more than half of its bm rows are valid (both token halves
 // of the block multiply) and 7 otherwise (one half multiplies; streaming its weights still takes most
 // of the time). Within a range the blocks of that XCD take tiles in order from a counter.
-__global__ __launch_bounds__(256) void ffn_schedule_mfma(const int32_t* __restrict__ offsets, int E, int T, int bm,
+// Exclusive prefix sum over the 512 threads of a block (buf: 512 entries of LDS, reusable on return).
+__device__ __forceinline__ long long block_exclusive_scan(long long v, long long* buf) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int o = 1; o < 512; o <<= 1) {
+    const long long add = t >= o ? buf[t - o] : 0;
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  const long long incl = buf[t];
+  __syncthreads();
+  return incl - v;
+}
+
+// One thread per group (routed experts 0..E-1, the shared group E): its M tiles and the cost of one row
+// of N tiles, then block-wide scans give every group its first tile and the cost before it, and the
+// group holding a boundary's cost finds the boundary tile within itself.
+__global__ __launch_bounds__(512) void ffn_schedule_mfma(const int32_t* __restrict__ offsets, int E, int T, int bm,
                                                          int ntr0, int nts0, int ntr1, int nts1,
                                                          int32_t* __restrict__ mt_prefix, int32_t* __restrict__ xrange,
                                                          int32_t* __restrict__ xcount) {
-  __shared__ int32_t s_mt[257], s_cost[257];
-  const int t = threadIdx.x;
-  auto column_cost = [&](int n, int& mt) {     // M tiles of a group with n rows and the cost of one N column
+  __shared__ long long buf[512];
+  __shared__ long long s_tot[2];
+  const int g = threadIdx.x;
+  const bool grp = g <= E;
+  auto tile_cost = [&](int n, int m) { return min(bm, n - m * bm) > bm / 2 ? 10 : 7; };
+  int n = 0, mt = 0, S = 0;
+  if (grp) {
+    n = g < E ? offsets[g + 1] - offsets[g] : T;
     mt = cdiv(n, bm);
-    int c = 0;
-    for (int m = 0; m < mt; ++m) c += min(bm, n - m * bm) > bm / 2 ? 10 : 7;
-    return c;
-  };
-  for (int g = t; g <= E; g += 256) {
-    int mt;
-    const int n = g < E ? offsets[g + 1] - offsets[g] : T;
-    s_cost[g] = column_cost(n, mt);
-    s_mt[g] = mt;
+    for (int m = 0; m < mt; ++m) S += tile_cost(n, m);
   }
-  if (t < 16) xcount[t] = 0;
-  __syncthreads();
-  if (t == 0) {
-    int m = 0;
-    for (int g = 0; g < E; ++g) {
-      mt_prefix[g] = m;
-      m += s_mt[g];
+  if (g < 16) xcount[g] = 0;
+  // M tiles before each routed group; for g = E this is their total
+  const long long mpre = block_exclusive_scan(g < E ? mt : 0, buf);
+  if (grp) mt_prefix[g] = (int)mpre;
+  for (int l = 0; l < 2; ++l) {
+    const int nt = g < E ? (l ? ntr1 : ntr0) : (l ? nts1 : nts0);
+    const long long C = grp ? (long long)nt * S : 0;       // cost of the group's tiles
+    const long long ntl = grp ? (long long)nt * mt : 0;    // and their number
+    const long long before = block_exclusive_scan(C, buf);
+    const long long id0 = block_exclusive_scan(ntl, buf);
+    if (g == E) {
+      s_tot[0] = before + C;
+      s_tot[1] = id0 + ntl;
     }
-    mt_prefix[E] = m;
-  }
-  if (t < 2) {
-    const int ntr = t == 0 ? ntr0 : ntr1, nts = t == 0 ? nts0 : nts1;
-    long long total = 0;
-    int tiles = 0;
-    for (int g = 0; g <= E; ++g) {
-      const int nt = g < E ? ntr : nts;
-      total += (long long)nt * s_cost[g];
-      tiles += nt * s_mt[g];
+    __syncthreads();
+    const long long total = s_tot[0];
+    int32_t* r = xrange + 9 * l;
+    if (g == 0) {
+      r[0] = 0;
+      r[8] = (int)s_tot[1];
     }
-    int32_t* r = xrange + 9 * t;
-    r[0] = 0;
-    r[8] = tiles;
-    // boundary x: the first tile whose preceding cost reaches x * total / 8. Within a group every N column
-    // costs s_cost[g]; the boundary's column follows by division and its M tile by a scan of one column.
-    int x = 1, id = 0;
-    long long before = 0;
-    for (int g = 0; g <= E && x < 8; ++g) {
-      const int nt = g < E ? ntr : nts, mt = s_mt[g], S = s_cost[g];
-      const int n = g < E ? offsets[g + 1] - offsets[g] : T;
-      const long long gend = before + (long long)nt * S;
-      while (x < 8 && total * x / 8 <= gend) {
-        const long long off = total * x / 8 - before;
-        if (off <= 0 || S == 0) {
-          r[x++] = id;
-          continue;
-        }
-        const int c0 = (int)(off / S);
-        const long long rem = off - (long long)c0 * S;
+    // boundary x: the first tile whose preceding cost reaches x * total / 8. The groups with tiles split
+    // (0, total] into the intervals (before, before + C]; the owner scans its rows of nt equal tiles (N
+    // fastest within an M tile) and divides within the row.
+    for (int x = 1; x < 8; ++x) {
+      const long long tgt = total * x / 8;
+      if (tgt <= 0) {
+        if (g == 0) r[x] = 0;
+        continue;
+      }
+      if (C > 0 && before < tgt && tgt <= before + C) {
+        const long long off = tgt - before;
         int mi = 0;
         long long cum = 0;
-        while (mi < mt && cum < rem) {
-          cum += min(bm, n - mi * bm) > bm / 2 ? 10 : 7;
-          ++mi;
-        }
-        r[x++] = id + c0 * mt + mi;
+        while (mi < mt && cum + (long long)nt * tile_cost(n, mi) < off) cum += (long long)nt * tile_cost(n, mi++);
+        const int ni = mi < mt ? (int)((off - cum + tile_cost(n, mi) - 1) / tile_cost(n, mi)) : 0;
+        r[x] = (int)(id0 + (long long)mi * nt + ni);
       }
-      before = gend;
-      id += nt * mt;
     }
-    while (x < 8) r[x++] = tiles;
+    __syncthreads();   // s_tot is written again by the next launch's totals
   }
 }
 
 hipError_t launch_schedule_mfma(const int32_t* offsets, int E, int T, int bm, const int (&nt_r)[2], const int (&nt_s)[2],
                                 int32_t* mt_prefix, int32_t* xrange, int32_t* xcount, hipStream_t s) {
-  ffn_schedule_mfma<<<1, 256, 0, s>>>(offsets, E, T, bm, nt_r[0], nt_s[0], nt_r[1], nt_s[1], mt_prefix, xrange, xcount);
+  ffn_schedule_mfma<<<1, 512, 0, s>>>(offsets, E, T, bm, nt_r[0], nt_s[0], nt_r[1], nt_s[1], mt_prefix, xrange, xcount);
   return hipGetLastError();
 }
 

@@ -17,11 +17,31 @@ struct RouteArgs {
   float* z;               // [T, E] fp32 logits
   double* z64;            // [T, E] fp64 logits of rechecked tokens (compacted)
   uint16_t* wg_split;     // [3, E, d] bf16 parts of w_gate (MFMA logits)
+  double* zpart;          // [ksplit, T, E] fp64 partial logits over slices of d (vector-ALU logits)
+  int ksplit, klen;       // slices of d and their length (a multiple of 32); ksplit 1 writes z directly
   int* recheck_count;
   int* recheck_list;      // [T]
   int32_t* topk_idx;
   float* topk_w;
 };
+
+// Slices of d for the vector-ALU router logits: enough 64x64 blocks to cover the chip when T and E are
+// small (a decode step), each slice at least 128 long, partial sums at most 64 MiB. Sets klen.
+inline int router_ksplit(int T, int E, int d, int& klen) {
+  const long long blocks = (long long)((T + 63) / 64) * ((E + 63) / 64);
+  if (blocks <= 0 || d <= 0) {   // no tokens: nothing to split
+    klen = d;
+    return 1;
+  }
+  long long s = (512 + blocks - 1) / blocks;
+  s = s < 1 ? 1 : s;
+  const long long smax = (d + 127) / 128;
+  s = s > smax ? smax : s;
+  while (s > 1 && s * T * (long long)E * 8 > (64LL << 20)) s /= 2;
+  const int per = (int)((d + s - 1) / s);
+  klen = (per + 31) / 32 * 32;
+  return (d + klen - 1) / klen;
+}
 
 struct DispatchArgs {
   const int32_t* topk_idx;

@@ -12,29 +12,33 @@ namespace moe {
 // ------------------------------------------------------------------ logits on the vector ALUs
 // z[t, e] = sum_k u[t, k] * wg[e, k] + off[e]; 64 tokens x 64 experts per block, 4 x 4 per thread.
 // The products of fp32 / bf16 inputs are exact in fp64 and accumulate in fp64 (same vector rate as
-// unpacked fp32); z is rounded to fp32 once.
+// unpacked fp32); z is rounded to fp32 once. With few tokens (a decode step) blockIdx.z takes one slice
+// [z klen, (z + 1) klen) of d and stores its fp64 partial sum, and router_logits_sum adds the slices in
+// order, so the result does not depend on how the blocks are scheduled.
 template <typename TU>
 __global__ __launch_bounds__(256) void router_logits_valu(const TU* __restrict__ u, const float* __restrict__ wg,
                                                           const float* __restrict__ off, int T, int E, int d,
-                                                          float* __restrict__ z, int* __restrict__ recheck_count) {
+                                                          int klen, float* __restrict__ z, double* __restrict__ zpart,
+                                                          int* __restrict__ recheck_count) {
   __shared__ float As[32][68];
   __shared__ float Bs[32][68];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *recheck_count = 0;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *recheck_count = 0;
   const int tx = tid & 15, ty = tid >> 4;
   double acc[4][4] = {};
   const int lr = tid >> 2, lk = (tid & 3) * 8;
-  for (int k0 = 0; k0 < d; k0 += 32) {
+  const int kb = blockIdx.z * klen, ke = min(d, kb + klen);
+  for (int k0 = kb; k0 < ke; k0 += 32) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int k = k0 + lk + i;
       float a = 0.f, b = 0.f;
-      if (t0 + lr < T && k < d) {
+      if (t0 + lr < T && k < ke) {
         if constexpr (sizeof(TU) == 2) a = bf16_to_f32(u[(size_t)(t0 + lr) * d + k]);
         else a = u[(size_t)(t0 + lr) * d + k];
       }
-      if (e0 + lr < E && k < d) b = wg[(size_t)(e0 + lr) * d + k];
+      if (e0 + lr < E && k < ke) b = wg[(size_t)(e0 + lr) * d + k];
       As[lk + i][lr] = a;
       Bs[lk + i][lr] = b;
     }
@@ -60,8 +64,21 @@ __global__ __launch_bounds__(256) void router_logits_valu(const TU* __restrict__
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + tx * 4 + j;
-      if (e < E) z[(size_t)t * E + e] = (float)(acc[i][j] + (off ? (double)off[e] : 0.0));
+      if (e >= E) continue;
+      if (zpart) zpart[((size_t)blockIdx.z * T + t) * E + e] = acc[i][j];
+      else z[(size_t)t * E + e] = (float)(acc[i][j] + (off ? (double)off[e] : 0.0));
     }
+  }
+}
+
+// z[t, e] = fp32(sum over slices s = 0.. of zpart[s, t, e] + off[e]), the slices added in order.
+__global__ __launch_bounds__(256) void router_logits_sum(const double* __restrict__ zpart, int ksplit, int T, int E,
+                                                         const float* __restrict__ off, float* __restrict__ z) {
+  const size_t n = (size_t)T * E;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    double acc = 0.0;
+    for (int s = 0; s < ksplit; ++s) acc += zpart[(size_t)s * n + i];
+    z[i] = (float)(acc + (off ? (double)off[i % E] : 0.0));
   }
 }
 
@@ -443,12 +460,24 @@ __global__ __launch_bounds__(256) void router_recheck_select(const double* __res
 // ------------------------------------------------------------------ launchers
 hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  dim3 g1(cdiv(a.T, 64), cdiv(a.E, 64));
-  if (a.u_bf16) {
-    if (a.use_mfma) launch_router_logits_mfma(a, s);
-    else router_logits_valu<uint16_t><<<g1, 256, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.T, a.E, a.d, a.z, a.recheck_count);
-  } else {
-    router_logits_valu<float><<<g1, 256, 0, s>>>((const float*)a.u, a.wg, a.off, a.T, a.E, a.d, a.z, a.recheck_count);
+  if (a.u_bf16 && a.use_mfma) {
+    launch_router_logits_mfma(a, s);
+    return hipGetLastError();
+  }
+  const bool split = a.ksplit > 1;
+  const int klen = split ? a.klen : a.d;
+  double* zp = split ? a.zpart : nullptr;
+  dim3 g1(cdiv(a.T, 64), cdiv(a.E, 64), split ? a.ksplit : 1);
+  if (a.u_bf16)
+    router_logits_valu<uint16_t><<<g1, 256, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.T, a.E, a.d, klen, a.z, zp,
+                                                    a.recheck_count);
+  else
+    router_logits_valu<float><<<g1, 256, 0, s>>>((const float*)a.u, a.wg, a.off, a.T, a.E, a.d, klen, a.z, zp,
+                                                 a.recheck_count);
+  if (split) {
+    const long long n = (long long)a.T * a.E;
+    const long long nb = (n + 255) / 256;
+    router_logits_sum<<<(unsigned)(nb < 2048 ? nb : 2048), 256, 0, s>>>(a.zpart, a.ksplit, a.T, a.E, a.off, a.z);
   }
   return hipGetLastError();
 }
