@@ -82,6 +82,15 @@ def roofline(work, ms, peak_mfma):
             "frac": round(ach / (peak_mfma / 1e12), 4), "traffic": None}
 
 
+def gateup_kernel_name(w):
+    """The kernel that runs the gate/up projection of workload w (the library picks it from the config)."""
+    if w.wdt == "f32":
+        return "grouped_gemm_simt gate/up"
+    if w.wdt == "fp8" and w.T <= 64:
+        return "grouped_gemm_decode gate/up+SwiGLU"
+    return "grouped_gemm_mfma gate/up+SwiGLU"
+
+
 def profiled_traffic(workload):
     """HBM bytes per launch of the two grouped GEMM kernels from the committed counter profile of this
     workload (profiles/traffic_<workload>.json), or None when the kernel source changed since."""
@@ -231,8 +240,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d_model": w.d, "routed": w.E, "shared": w.Ks, "top_k": w.K,
                    "inter_dim": w.f, "gate": w.gate, "renorm": w.renorm, "weights": w.wdt, "act": w.act,
                    "bias_update": w.gamma is not None},
-        "roofline": dict(kernel="grouped_gemm_mfma gate/up+SwiGLU" if w.wdt != "f32" else "grouped_gemm_simt gate/up",
-                         **roofline(gwork, stage["gateup"], peak)),
+        "roofline": dict(kernel=gateup_kernel_name(w), **roofline(gwork, stage["gateup"], peak)),
         "algorithmic_bytes": {"gateup": int(gwork["bytes"]), "down": int(dwork["bytes"])},
         "grouped_gemm_tflops": round(gemm_tflops, 1),
         "grouped_gemm_mfma_frac": round(gemm_tflops * 1e12 / peak, 4),

@@ -247,11 +247,13 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   int32_t* xrange = reinterpret_cast<int32_t*>(base + L.xsched);
   int32_t* xcount = xrange + 2 * 9;
   const int fs = c->n_shared * c->inter_dim;
-  if (mfma) {
+  // a decode-sized E4M3 batch streams the touched experts' weights with its own kernels (no tile list)
+  const bool decode = fp8 && c->T <= gemm_decode_max_tokens();
+  if (mfma && !decode) {
     const int nt_r[2] = {c->inter_dim / 128, c->d_model / 256}, nt_s[2] = {fs / 128, fs > 0 ? c->d_model / 256 : 0};
     MOE_TRY(hip_status(launch_schedule_mfma(offsets, c->n_routed, c->T, bm, nt_r, nt_s, mt_prefix, xrange, xcount, s),
                        "schedule launch"));
-  } else {
+  } else if (!mfma) {
     MOE_TRY(hip_status(launch_schedule(offsets, c->n_routed, bm, mt_prefix, s), "schedule launch"));
   }
   GemmArgs g{};
@@ -288,7 +290,9 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   g.out_scale_routed = reinterpret_cast<float*>(base + L.as_r);
   g.out_scale_shared = reinterpret_cast<float*>(base + L.as_s);
   const long long rows = (long long)c->T * c->top_k;
-  if (mfma) {
+  if (decode) {
+    MOE_TRY(hip_status(launch_gemm_decode(g, true, s), "gate/up GEMM launch"));
+  } else if (mfma) {
     const int grid = device_cus() / 8 * 8;
     MOE_TRY(hip_status(launch_gemm_mfma(g, fp8, true, grid, s), "gate/up GEMM launch"));
   } else {
@@ -313,7 +317,9 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   g.out_scale_shared = nullptr;
   g.xrange = xrange + 9;
   g.xcount = xcount + 8;
-  if (mfma) {
+  if (decode) {
+    MOE_TRY(hip_status(launch_gemm_decode(g, false, s), "down GEMM launch"));
+  } else if (mfma) {
     const int grid = device_cus() / 8 * 8;
     MOE_TRY(hip_status(launch_gemm_mfma(g, fp8, false, grid, s), "down GEMM launch"));
   } else {

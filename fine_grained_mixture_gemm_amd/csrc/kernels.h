@@ -90,6 +90,9 @@ hipError_t launch_schedule_mfma(const int32_t* offsets, int E, int T, int bm, co
                                 int32_t* mt_prefix, int32_t* xrange, int32_t* xcount, hipStream_t s);
 int gemm_mfma_bm();
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s);
+// E4M3 grouped GEMMs for batches of at most gemm_decode_max_tokens() tokens (weight streaming)
+int gemm_decode_max_tokens();
+hipError_t launch_gemm_decode(const GemmArgs& a, bool gateup, hipStream_t s);
 int gemm_simt_bm();
 hipError_t launch_gemm_simt(const GemmArgs& a, bool gateup, int max_tiles, hipStream_t s);
 hipError_t launch_combine(const void* u, bool bf16, const void* y_routed, const void* y_shared, bool y_bf16,

@@ -24,6 +24,11 @@ SMALL = {
     "fp8_sigmoid_ragged": W["v3_fp8"].replace(name="fp8_sigmoid_ragged", T=333, d=512, E=20, K=4),
     "fp8_k_equals_e": W["v3_fp8"].replace(name="fp8_k_equals_e", T=70, d=256, E=4, K=4),
     "fp8_one_token": W["v3_fp8"].replace(name="fp8_one_token", T=1, d=256, E=32, K=8),
+    # batches of at most 64 tokens take the E4M3 decode kernels: groups spanning 3 and 4 token tiles,
+    # two shared experts (shared inner dim 2 f)
+    "fp8_decode_3tiles": W["v3_fp8"].replace(name="fp8_decode_3tiles", T=64, d=512, E=6, K=4),
+    "fp8_decode_2shared": W["v3_fp8"].replace(name="fp8_decode_2shared", T=40, d=512, E=16, Ks=2, K=6),
+    "fp8_decode_k_equals_e": W["v3_fp8"].replace(name="fp8_decode_k_equals_e", T=64, d=256, E=4, K=4),
     "f32_sigmoid_norenorm": W["tiny_f32"].replace(name="f32_sigmoid_norenorm", gate="sigmoid_bias", renorm=False,
                                                   bias_range=0.1, T=77, E=9, K=3),
 }
