@@ -105,6 +105,32 @@ def profiled_traffic(workload):
     return rec
 
 
+def time_balance_stats(moe, L, w, ws, reps=20):
+    """Time moe_balance_stats (f, P, expert-level and sequence-wise losses) on the router outputs of the
+    workload; not part of the step. Sequences of 4096 tokens when they divide T, else one sequence."""
+    import torch
+    seq = 4096 if w.T % 4096 == 0 else w.T
+    z = torch.empty((w.T, w.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
+    gw = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
+    moe.moe_router_logits(L.cfg, L.layer, L.t["u"], z, ws)
+    moe.moe_route(L.cfg, L.layer, L.t["u"], L.t["bias"], idx, gw, ws)
+    f = torch.empty(w.E, dtype=torch.float32, device="cuda")
+    P = torch.empty_like(f)
+    loss = torch.empty(2, dtype=torch.float32, device="cuda")
+    run = lambda: moe.moe_balance_stats(L.cfg, z, idx, seq, 0.003, 0.0001, f, P, loss, ws)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return {"ms": round(e0.elapsed_time(e1) / reps, 4), "seq_len": seq,
+            "loss_expert": float(loss[0]), "loss_seq": float(loss[1])}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -249,6 +275,7 @@ def main():
         "touched_experts": touched,
         "setup_s": round(setup_s, 1),
     }
+    out["balance_stats"] = time_balance_stats(moe, L, w, ws)
     prof = profiled_traffic(w.name)
     if prof is not None:
         out["roofline"]["traffic"] = round(prof["gateup"]["traffic_bytes"])

@@ -60,6 +60,7 @@ _SIGS = {
     "moe_combine": [_CP, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_forward": [_CP, _LP, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_update_bias": [_CP, _vp, _f32, _vp, _vp],
+    "moe_balance_stats": [_CP, _vp, _vp, _i32, _f32, _f32, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_quantize_weights": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
     "moe_quantize_act": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
     "moe_set_timing_events": [_vp, _i32],
@@ -148,6 +149,12 @@ def moe_forward(cfg, layer, u, bias, h, topk_idx, counts, ws, stream=None):
 
 def moe_update_bias(cfg, counts, gamma, bias, stream=None):
     _call("moe_update_bias", ctypes.byref(cfg), _dev(counts), float(gamma), _dev(bias), _stream(stream))
+
+
+def moe_balance_stats(cfg, z, topk_idx, seq_len, alpha_expert, alpha_seq, f, P, loss, ws, stream=None):
+    _call("moe_balance_stats", ctypes.byref(cfg), _dev(z), _dev(topk_idx), int(seq_len), float(alpha_expert),
+          float(alpha_seq), _dev(f), _dev(P), _dev(loss), _dev(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+          _stream(stream))
 
 
 def moe_quantize_weights(w, q, scales, stream=None):

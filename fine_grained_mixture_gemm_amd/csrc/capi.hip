@@ -96,6 +96,7 @@ struct Layout {
   size_t chunk_counts, chunk_base, mt_prefix, xsched;
   size_t uq, us, a_r, a_s, as_r, as_s;
   size_t f_idx, f_w, f_counts, f_offsets, f_perm, f_rowof, f_yr, f_ys;
+  size_t bal_psum, bal_cnt, bal_seqp, bal_seqn, bal_seq;
   size_t total;
 };
 
@@ -139,6 +140,13 @@ Layout layout(const moe_config* c) {
   L.f_rowof = take(rows * 4);
   L.f_yr = take(rows * d * esz_y(c));
   L.f_ys = take(T * d * esz_y(c));
+  const size_t bch = balance_chunks_for(c->T);
+  L.bal_psum = take(bch * E * 8);
+  L.bal_cnt = take(bch * E * 4);
+  const size_t bsq = balance_sequences_max(c->T);
+  L.bal_seqp = take(bsq * E * 8);
+  L.bal_seqn = take(bsq * E * 4);
+  L.bal_seq = take(bsq * 8);
   L.total = off + 256;   // room to align the caller's base pointer up to 256 bytes
   return L;
 }
@@ -459,6 +467,39 @@ moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float g
   if (!counts || !bias) return fail(MOE_ERR_INVALID_ARG, "counts / bias is NULL");
   return hip_status(launch_bias_update(counts, cfg->n_routed, (long long)cfg->T * cfg->top_k, gamma, bias, stream),
                     "bias update launch");
+}
+
+moe_status moe_balance_stats(const moe_config* cfg, const float* z, const int32_t* topk_idx, int32_t seq_len,
+                             float alpha_expert, float alpha_seq, float* f, float* P, float* loss, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (seq_len <= 0 || cfg->T % seq_len)
+    return fail(MOE_ERR_INVALID_ARG, "seq_len=%d must be positive and divide T=%d", seq_len, cfg->T);
+  if (seq_len != cfg->T && seq_len % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "seq_len=%d must equal T or be a multiple of 64", seq_len);
+  if (cfg->T > 0 && (!z || !topk_idx || !f || !P || !loss)) return fail(MOE_ERR_INVALID_ARG, "z / topk_idx / f / P / loss is NULL");
+  uint8_t* base;
+  Layout L;
+  MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
+  BalanceArgs a{};
+  a.z = z;
+  a.idx = topk_idx;
+  a.T = cfg->T;
+  a.E = cfg->n_routed;
+  a.K = cfg->top_k;
+  a.gate = cfg->gate;
+  a.seq_len = seq_len;
+  a.alpha_expert = alpha_expert;
+  a.alpha_seq = alpha_seq;
+  a.psum = reinterpret_cast<double*>(base + L.bal_psum);
+  a.cnt = reinterpret_cast<int32_t*>(base + L.bal_cnt);
+  a.seq_p = reinterpret_cast<double*>(base + L.bal_seqp);
+  a.seq_n = reinterpret_cast<int32_t*>(base + L.bal_seqn);
+  a.seq_term = reinterpret_cast<double*>(base + L.bal_seq);
+  a.f = f;
+  a.P = P;
+  a.loss = loss;
+  return hip_status(launch_balance_stats(a, stream), "balance statistics launch");
 }
 
 moe_status moe_quantize_weights(const float* w, int32_t batch, int32_t rows, int32_t cols, uint8_t* q, float* scales,

@@ -54,6 +54,22 @@ struct DispatchArgs {
   int32_t* row_of;
 };
 
+// Load-balance statistics of one routed batch.
+struct BalanceArgs {
+  const float* z;         // [T, E] router logits
+  const int32_t* idx;     // [T, K] selected experts
+  int T, E, K, gate, seq_len;
+  float alpha_expert, alpha_seq;
+  double* psum;           // [chunks, E] per-chunk sums of routing probabilities
+  int32_t* cnt;           // [chunks, E] per-chunk selection counts
+  double* seq_p;          // [T / seq_len, E] per-sequence sums of routing probabilities
+  int32_t* seq_n;         // [T / seq_len, E] per-sequence selection counts
+  double* seq_term;       // [T / seq_len] sum_i f_i P_i of each sequence
+  float* f;               // [E] out
+  float* P;               // [E] out
+  float* loss;            // [2] out: expert-level, sequence-wise
+};
+
 // One grouped GEMM launch (gate/up + SwiGLU, or down) over the E routed groups and the shared group.
 struct GemmArgs {
   int E, T, d, f, fs;
@@ -90,6 +106,9 @@ hipError_t launch_schedule_mfma(const int32_t* offsets, int E, int T, int bm, co
                                 int32_t* mt_prefix, int32_t* xrange, int32_t* xcount, hipStream_t s);
 int gemm_mfma_bm();
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s);
+int balance_chunks_for(int T);
+int balance_sequences_max(int T);   // sequences of T tokens when seq_len is T or a multiple of 64
+hipError_t launch_balance_stats(const BalanceArgs& a, hipStream_t s);
 // E4M3 grouped GEMMs for batches of at most gemm_decode_max_tokens() tokens (weight streaming)
 int gemm_decode_max_tokens();
 hipError_t launch_gemm_decode(const GemmArgs& a, bool gateup, hipStream_t s);

@@ -152,6 +152,25 @@ moe_status moe_forward(const moe_config* cfg, const moe_layer* layer, const void
 moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* bias,
                            hipStream_t stream);
 
+/* Load-balance statistics of one routed batch (DeepSeek Technical Report: MoE Architecture, 1.2
+ * expert-level balance loss L_ExpBal = alpha_1 * sum_i f_i * P_i, alpha_1 = 0.003 in 2.3; 3.3 the V3
+ * sequence-wise balance loss, weight 0.0001, formula not printed). Readings: f_i = (tokens whose top-K
+ * holds i) / T, with no E/K normalisation (sum_i f_i = K); P_i = mean over tokens of the probability of
+ * expert i over all routed experts: softmax(z) in softmax mode, sigmoid(z) / sum_j sigmoid(z_j) in
+ * sigmoid mode (the selection bias is not part of it); the sequence-wise loss is alpha_seq times the
+ * mean over the T / seq_len sequences of sum_i f_i^b P_i^b taken within each sequence.
+ *  z        [T, E] fp32: router logits, as moe_router_logits returns them.
+ *  topk_idx [T, K] int32: the selection, as moe_route returns it.
+ *  seq_len  tokens per sequence (consecutive tokens): T itself, or a multiple of 64 that divides T
+ *           (otherwise MOE_ERR_INVALID_ARG if it does not divide T, MOE_ERR_UNSUPPORTED if it is not a
+ *           multiple of 64).
+ *  f, P     [E] fp32 out; loss [2] fp32 out: loss[0] = alpha_expert * sum f P, loss[1] = the
+ *           sequence-wise loss. All sums run in fp64 in a fixed order (the result is deterministic).
+ *  ws / ws_bytes: the layer workspace (moe_workspace_size); device pointers throughout. */
+moe_status moe_balance_stats(const moe_config* cfg, const float* z, const int32_t* topk_idx, int32_t seq_len,
+                             float alpha_expert, float alpha_seq, float* f, float* P, float* loss, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
 /* Offline weight preparation (DeepSeek Technical Report: MoE Architecture, 3.6, 128x128 weight blocks):
  * quantizes `batch` fp32 matrices w [batch, rows, cols] (rows, cols multiples of 128) to E4M3 codes
  * q [batch, rows, cols] uint8 and block scales [batch, rows/128, cols/128] fp32 with

@@ -97,6 +97,21 @@ def test_null_pointers_and_workspace_errors():
     assert lib.moe_set_timing_events(None, 0) == moe.MOE_OK
 
 
+def test_balance_stats_argument_errors():
+    # every check runs before any launch: non-null dummy pointers are never dereferenced
+    cfg = _cfg(T=256)
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    lib.moe_balance_stats.argtypes = ([ctypes.POINTER(moe.moe_config), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.c_float, ctypes.c_float] + [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p])
+    call = lambda seq, z=16, ws=16, nbytes=1 << 31: lib.moe_balance_stats(ctypes.byref(cfg), z, 16, seq, 0.003, 1e-4, 16, 16, 16, ws, nbytes, None)
+    assert call(0) == moe.MOE_ERR_INVALID_ARG
+    assert call(100) == moe.MOE_ERR_INVALID_ARG          # does not divide T
+    assert call(32) == moe.MOE_ERR_UNSUPPORTED           # divides T, not a multiple of 64
+    assert call(64, z=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(64, nbytes=1024) == moe.MOE_ERR_WORKSPACE
+    assert call(256, ws=None) == moe.MOE_ERR_WORKSPACE
+
+
 def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
