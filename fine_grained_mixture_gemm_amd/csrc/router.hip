@@ -128,6 +128,14 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
   i32x4 Bst[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) Bst[q] = *reinterpret_cast<const i32x4*>(ub + boff[q]);
+  // centroid parts of the next stage are loaded while this stage multiplies
+  i32x4 A[3][2], An[3][2];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    A[p][0] = *reinterpret_cast<const i32x4*>(wp + p * n * 2);
+    A[p][1] = *reinterpret_cast<const i32x4*>(wp + p * n * 2 + 64);
+  }
+  const int tr = lane & 15, g = lane >> 4;
   for (int kb = 0; kb < nst; ++kb) {
     uint8_t* buf = lds[kb & 1];
 #pragma unroll
@@ -139,26 +147,34 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
     if (kb + 1 < nst) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) Bst[q] = *reinterpret_cast<const i32x4*>(ub + (size_t)(kb + 1) * 128 + boff[q]);
-    }
-    i32x4 A[3][2];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const uint8_t* pp = wp + p * n * 2 + kb * 128;
-      A[p][0] = *reinterpret_cast<const i32x4*>(pp);
-      A[p][1] = *reinterpret_cast<const i32x4*>(pp + 64);
+      for (int p = 0; p < 3; ++p) {
+        const uint8_t* pp = wp + p * n * 2 + (kb + 1) * 128;
+        An[p][0] = *reinterpret_cast<const i32x4*>(pp);
+        An[p][1] = *reinterpret_cast<const i32x4*>(pp + 64);
+      }
     }
-    const int tr = lane & 15, g = lane >> 4;
+    i32x4 b[8][2];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = 16 * j + tr;
-      const i32x4 b0 = *reinterpret_cast<const i32x4*>(buf + row * 128 + ((g ^ (row & 7)) * 16));
-      const i32x4 b1 = *reinterpret_cast<const i32x4*>(buf + row * 128 + (((4 + g) ^ (row & 7)) * 16));
+      b[j][0] = *reinterpret_cast<const i32x4*>(buf + row * 128 + ((g ^ (row & 7)) * 16));
+      b[j][1] = *reinterpret_cast<const i32x4*>(buf + row * 128 + (((4 + g) ^ (row & 7)) * 16));
+    }
+    // the eight token tiles innermost: consecutive MFMAs update different accumulators
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[p][h]),
+                                                           __builtin_bit_cast(bf16x8, b[j][h]), acc[j], 0, 0, 0);
+    if (kb + 1 < nst) {
 #pragma unroll
       for (int p = 0; p < 3; ++p) {
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[p][0]),
-                                                         __builtin_bit_cast(bf16x8, b0), acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[p][1]),
-                                                         __builtin_bit_cast(bf16x8, b1), acc[j], 0, 0, 0);
+        A[p][0] = An[p][0];
+        A[p][1] = An[p][1];
       }
     }
   }
@@ -288,9 +304,10 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, 
 
 // ------------------------------------------------------------------ fp64 recheck of close tokens
 // Pass 1: fp64 logits of the flagged tokens. One block per routed expert e holds centroid row e in
-// registers (each thread every 256th element, as fp64), then takes the flagged tokens 8 at a time: their
-// u rows are copied into LDS with wide loads (all in flight together) and each of the 8 dot products is
-// reduced in fp64. Products of the stored inputs are exact in fp64.
+// registers (each thread every 256th element, as fp64) and takes the flagged tokens 8 at a time, reading
+// their u elements straight from memory (every element is used once per block, so there is nothing to
+// stage; the flagged rows stay in L2 for the other blocks); each of the 8 dot products is reduced in
+// fp64. Products of the stored inputs are exact in fp64.
 constexpr int kRecheckThreads = 256;
 constexpr int kRecheckMaxD = 8192;
 constexpr int kRecheckPer = kRecheckMaxD / kRecheckThreads;   // centroid elements per thread (32)
@@ -303,53 +320,38 @@ __global__ __launch_bounds__(kRecheckThreads) void router_recheck_logits(const T
                                                                          const int* __restrict__ recheck_count,
                                                                          const int* __restrict__ recheck_list,
                                                                          double* __restrict__ z64) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t rl_lds[];   // [kRecheckBatch][d] of TU
   __shared__ double part[kRecheckBatch][kRecheckThreads / 64];
   const int n = *recheck_count;
   if (n == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  TU* urows = reinterpret_cast<TU*>(rl_lds);
-  constexpr int V = 16 / sizeof(TU);                    // elements per 16-byte copy
   for (int e = blockIdx.x; e < E; e += gridDim.x) {
+    // indices past d are clamped (no branches, so every load can be in flight at once); their centroid
+    // values are zero and add nothing
     double w[kRecheckPer];
 #pragma unroll
     for (int i = 0; i < kRecheckPer; ++i) {
       const int k = tid + kRecheckThreads * i;
-      w[i] = k < d ? (double)wg[(size_t)e * d + k] : 0.0;
+      const double v = (double)wg[(size_t)e * d + min(k, d - 1)];
+      w[i] = k < d ? v : 0.0;
     }
     const double o = off ? (double)off[e] : 0.0;
     for (int q0 = 0; q0 < n; q0 += kRecheckBatch) {
       const int nb = min(kRecheckBatch, n - q0);
-      __syncthreads();                                  // previous batch's LDS reads are done
-      if (d % V == 0) {                                 // rows stay 16-byte aligned
-        for (int c = tid; c < nb * (d / V); c += kRecheckThreads) {
-          const int b = c / (d / V), k = (c % (d / V)) * V;
-          *reinterpret_cast<int4*>(urows + (size_t)b * d + k) =
-              *reinterpret_cast<const int4*>(u + (size_t)recheck_list[q0 + b] * d + k);
-        }
-      } else {
-        for (int c = tid; c < nb * d; c += kRecheckThreads) {
-          const int b = c / d, k = c % d;
-          urows[(size_t)b * d + k] = u[(size_t)recheck_list[q0 + b] * d + k];
-        }
-      }
-      __syncthreads();
       double acc[kRecheckBatch];
 #pragma unroll
-      for (int b = 0; b < kRecheckBatch; ++b) acc[b] = 0.0;
+      for (int b = 0; b < kRecheckBatch; ++b) {
+        acc[b] = 0.0;
+        if (b < nb) {
+          const TU* ur = u + (size_t)recheck_list[q0 + b] * d;
+          float x[kRecheckPer];
 #pragma unroll
-      for (int i = 0; i < kRecheckPer; ++i) {
-        const int k = tid + kRecheckThreads * i;
-        if (k < d) {
-#pragma unroll
-          for (int b = 0; b < kRecheckBatch; ++b) {
-            if (b < nb) {
-              double x;
-              if constexpr (sizeof(TU) == 2) x = (double)bf16_to_f32(urows[(size_t)b * d + k]);
-              else x = (double)urows[(size_t)b * d + k];
-              acc[b] = fma(x, w[i], acc[b]);
-            }
+          for (int i = 0; i < kRecheckPer; ++i) {
+            const int k = min(tid + kRecheckThreads * i, d - 1);
+            if constexpr (sizeof(TU) == 2) x[i] = bf16_to_f32(ur[k]);
+            else x[i] = ur[k];
           }
+#pragma unroll
+          for (int i = 0; i < kRecheckPer; ++i) acc[b] = fma((double)x[i], w[i], acc[b]);
         }
       }
 #pragma unroll
@@ -359,6 +361,7 @@ __global__ __launch_bounds__(kRecheckThreads) void router_recheck_logits(const T
       }
       __syncthreads();
       if (tid < nb) z64[(size_t)(q0 + tid) * E + e] = ((part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3])) + o;
+      __syncthreads();                                  // part is written again by the next batch
     }
   }
 }
@@ -493,18 +496,12 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   else
     router_topk<MOE_GATE_SIGMOID_BIAS><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.delta, a.topk_idx,
                                                           a.topk_w, a.recheck_count, a.recheck_list);
-  const size_t rl_bytes = (size_t)kRecheckBatch * a.d * (a.u_bf16 ? 2 : 4);
-  if (a.u_bf16) {
-    (void)hipFuncSetAttribute((const void*)router_recheck_logits<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)rl_bytes);
-    router_recheck_logits<uint16_t><<<a.E, kRecheckThreads, rl_bytes, s>>>((const uint16_t*)a.u, a.wg, a.off, a.E,
-                                                                            a.d, a.recheck_count, a.recheck_list, a.z64);
-  } else {
-    (void)hipFuncSetAttribute((const void*)router_recheck_logits<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)rl_bytes);
-    router_recheck_logits<float><<<a.E, kRecheckThreads, rl_bytes, s>>>((const float*)a.u, a.wg, a.off, a.E, a.d,
-                                                                         a.recheck_count, a.recheck_list, a.z64);
-  }
+  if (a.u_bf16)
+    router_recheck_logits<uint16_t><<<a.E, kRecheckThreads, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.E, a.d,
+                                                                     a.recheck_count, a.recheck_list, a.z64);
+  else
+    router_recheck_logits<float><<<a.E, kRecheckThreads, 0, s>>>((const float*)a.u, a.wg, a.off, a.E, a.d,
+                                                                  a.recheck_count, a.recheck_list, a.z64);
   if (a.gate == MOE_GATE_SOFTMAX)
     router_recheck_select<MOE_GATE_SOFTMAX><<<64, 256, 0, s>>>(a.z64, a.E, a.K, a.bias, a.renorm, a.recheck_count,
                                                                a.recheck_list, a.topk_idx, a.topk_w);
