@@ -56,7 +56,10 @@ __device__ __forceinline__ void e4m3_scales(float amax, float& s, float& inv) {
   }
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU(g) = g * sigmoid(g) with the hardware reciprocal (1 ulp) in place of an IEEE division; the result
+// is requantized (E4M3 or bf16) or compared at 1e-5 (fp32), far above that difference. Large negative g:
+// the reciprocal of +inf is 0, as the division would give.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // ------------------------------------------------------------------ wave reductions
 __device__ __forceinline__ float wave_max(float v) {
