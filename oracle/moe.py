@@ -61,14 +61,44 @@ def topk_select(key, K: int):
     return idx, gap
 
 
-def route(z, gate: str, K: int, bias=None, renorm: bool = False):
+def group_limit(key, n_groups: int, topk_groups: int):
+    """Device/node-limited routing ([TR] §2.3 device-limited routing, M = 3 devices; §3.2 and §3.8
+    node-limited routing, M = 4 nodes): a token's experts come from at most M groups.
+
+    Reading (the pages do not print the rule): the E experts form n_groups equal contiguous groups
+    (group of expert e = e // (E / n_groups)); a group's score is the largest key among its experts;
+    the M = topk_groups groups with the largest scores are kept (ties to the lower group index) and
+    the keys of every other group are masked to -inf before the top-K.
+    Returns (masked key [T, E], group gap [T]): the M-th largest group score minus the (M+1)-th
+    (inf when M == n_groups), the margin by which the group choice is decided.
+    """
+    key = np.asarray(key, dtype=np.float64)
+    T, E = key.shape
+    gsz = E // n_groups
+    gscore = key.reshape(T, n_groups, gsz).max(axis=2)
+    order = np.argsort(-gscore, axis=1, kind="stable")     # stable: equal scores keep ascending group
+    keep = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(keep, order[:, :topk_groups], True, axis=1)
+    masked = np.where(np.repeat(keep, gsz, axis=1), key, -np.inf)
+    if topk_groups < n_groups:
+        rows = np.arange(T)
+        ggap = gscore[rows, order[:, topk_groups - 1]] - gscore[rows, order[:, topk_groups]]
+    else:
+        ggap = np.full(T, np.inf)
+    return masked, ggap
+
+
+def route(z, gate: str, K: int, bias=None, renorm: bool = False, n_groups: int = 0, topk_groups: int = 0):
     """Selection and gates from the logits z [T, E].
 
     softmax ([TR] §2.3): p = Softmax(z); the K largest p are selected (p is monotone in z, so the key
     is z itself, which avoids ties created by rounding exp); gates g = p of the selected experts.
     sigmoid_bias ([TR] §3.3): s = Sigmoid(z); selected iff s_i + b_i is among the K largest of
     {s_j + b_j}; g' = s of the selected experts; g = g' / sum g' when renorm.
-    Returns dict(idx [T,K] int32 ascending, w [T,K] float64, gap [T], key [T,E], score [T,E]).
+    With n_groups > 0 the selection is first limited to topk_groups groups (group_limit); the gates are
+    computed as without the limit.
+    Returns dict(idx [T,K] int32 ascending, w [T,K] float64, gap [T], key [T,E], score [T,E]); gap is
+    the smaller of the top-K margin and the group margin.
     """
     z = np.asarray(z, dtype=np.float64)
     if gate == "softmax":
@@ -80,7 +110,14 @@ def route(z, gate: str, K: int, bias=None, renorm: bool = False):
         key = score + b[None, :]
     else:
         raise ValueError(gate)
-    idx, gap = topk_select(key, K)
+    if n_groups:
+        if z.shape[1] % n_groups or not 1 <= topk_groups <= n_groups or K > topk_groups * (z.shape[1] // n_groups):
+            raise ValueError("bad group limit")
+        masked, ggap = group_limit(key, n_groups, topk_groups)
+        idx, gap = topk_select(masked, K)
+        gap = np.minimum(gap, ggap)
+    else:
+        idx, gap = topk_select(key, K)
     w = np.take_along_axis(score, idx.astype(np.int64), axis=1)
     if renorm:
         w = w / w.sum(axis=1, keepdims=True)
