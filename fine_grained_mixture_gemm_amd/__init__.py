@@ -35,7 +35,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 
 class moe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("T", "d_model", "n_routed", "n_shared", "top_k", "inter_dim", "gate",
-                                                "renorm", "act_dtype", "w_dtype")]
+                                                "renorm", "act_dtype", "w_dtype", "n_groups", "topk_groups")]
 
 
 class moe_layer(ctypes.Structure):
@@ -99,8 +99,10 @@ def _call(name, *args):
         raise MoeError(name, st)
 
 
-def make_config(T, d_model, n_routed, n_shared, top_k, inter_dim, gate, renorm, act_dtype, w_dtype) -> moe_config:
-    return moe_config(T, d_model, n_routed, n_shared, top_k, inter_dim, gate, int(renorm), act_dtype, w_dtype)
+def make_config(T, d_model, n_routed, n_shared, top_k, inter_dim, gate, renorm, act_dtype, w_dtype, n_groups=0,
+                topk_groups=0) -> moe_config:
+    return moe_config(T, d_model, n_routed, n_shared, top_k, inter_dim, gate, int(renorm), act_dtype, w_dtype,
+                      n_groups, topk_groups)
 
 
 def make_layer(w13, w2, w_gate, ws13=None, ws2=None, w13_scale=None, w2_scale=None, ws13_scale=None,

@@ -67,6 +67,13 @@ moe_status check_cfg(const moe_config* c) {
   if (c->w_dtype != MOE_F32 && c->w_dtype != MOE_BF16 && c->w_dtype != MOE_FP8_E4M3)
     return fail(MOE_ERR_INVALID_ARG, "bad w_dtype %d", c->w_dtype);
   if (c->n_routed > 256) return fail(MOE_ERR_UNSUPPORTED, "n_routed=%d > 256 (one wave holds at most 256 keys)", c->n_routed);
+  if (c->n_groups != 0 || c->topk_groups != 0) {
+    if (c->n_groups < 1 || c->n_routed % c->n_groups || c->topk_groups < 1 || c->topk_groups > c->n_groups ||
+        c->top_k > c->topk_groups * (c->n_routed / c->n_groups))
+      return fail(MOE_ERR_INVALID_ARG, "bad group limit: n_groups=%d topk_groups=%d (E=%d K=%d)", c->n_groups,
+                  c->topk_groups, c->n_routed, c->top_k);
+    if (c->n_groups > 16) return fail(MOE_ERR_UNSUPPORTED, "n_groups=%d > 16", c->n_groups);
+  }
   if (c->top_k > 16) return fail(MOE_ERR_UNSUPPORTED, "top_k=%d > 16", c->top_k);
   if (c->d_model > 8192) return fail(MOE_ERR_UNSUPPORTED, "d_model=%d > 8192 (fp64 router recheck)", c->d_model);
   const bool pair_ok = (c->act_dtype == MOE_F32 && c->w_dtype == MOE_F32) ||
@@ -205,6 +212,8 @@ RouteArgs route_args(const moe_config* c, const moe_layer* l, const void* u, con
   a.K = c->top_k;
   a.gate = c->gate;
   a.renorm = c->renorm;
+  a.n_groups = c->n_groups;
+  a.topk_groups = c->topk_groups;
   a.delta = c->gate == MOE_GATE_SOFTMAX ? kRecheckDeltaSoftmax : kRecheckDeltaSigmoid;
   a.z = reinterpret_cast<float*>(base + L.z);
   a.z64 = reinterpret_cast<double*>(base + L.z64);

@@ -13,6 +13,7 @@ struct RouteArgs {
   const float* off;
   const float* bias;
   int T, E, d, K, gate, renorm;
+  int n_groups, topk_groups;   // group-limited routing (0: none)
   float delta;
   float* z;               // [T, E] fp32 logits
   double* z64;            // [T, E] fp64 logits of rechecked tokens (compacted)

@@ -234,9 +234,61 @@ __device__ __forceinline__ float wave_topk_f32(const float key[4], const bool va
   return kth - k1;
 }
 
+// Group-limited routing on one wave (DeepSeek Technical Report: MoE Architecture, 2.3 device-limited
+// routing; 3.2 / 3.8 node-limited routing). Lanes hold the keys of experts lane + 64 j (valid[j]: the
+// expert exists). The E experts form G equal contiguous groups; a group scores the largest key of its
+// experts; the M best groups are kept (ties to the lower group index) and valid[] is cleared for the
+// experts of every other group. Returns the M-th best group score minus the (M+1)-th (+inf when
+// M == G): the margin by which the group choice is decided.
+template <typename V>
+__device__ __forceinline__ V group_limit_wave(const V key[4], bool valid[4], int E, int G, int M, int lane) {
+  const V ninf = -__builtin_inf();
+  const int gsz = E / G;
+  V gsc = ninf;                          // lane g < G: score of group g
+  for (int g = 0; g < G; ++g) {
+    V m = ninf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (valid[j] && (lane + 64 * j) / gsz == g) m = key[j] > m ? key[j] : m;
+    for (int o = 32; o > 0; o >>= 1) {
+      const V om = __shfl_xor(m, o, 64);
+      m = om > m ? om : m;
+    }
+    if (lane == g) gsc = m;
+  }
+  bool cand = lane < G;
+  unsigned keep = 0;
+  V mth = 0, m1 = ninf;
+  const int rounds = M < G ? M + 1 : M;
+  for (int r = 0; r < rounds; ++r) {
+    V bv = cand ? gsc : ninf;
+    int bg = cand ? lane : 0x7FFFFFFF;
+    for (int o = 32; o > 0; o >>= 1) {
+      const V ov = __shfl_xor(bv, o, 64);
+      const int og = __shfl_xor(bg, o, 64);
+      if (ov > bv || (ov == bv && og < bg)) {
+        bv = ov;
+        bg = og;
+      }
+    }
+    if (r < M) {
+      keep |= 1u << bg;
+      if (lane == bg) cand = false;
+      mth = bv;
+    } else {
+      m1 = bv;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (valid[j] && !((keep >> ((lane + 64 * j) / gsz)) & 1u)) valid[j] = false;
+  return mth - m1;
+}
+
 template <int GATE>
 __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, int T, int E, int K,
-                                                   const float* __restrict__ bias, int renorm, float delta,
+                                                   const float* __restrict__ bias, int renorm, int G, int M,
+                                                   float delta,
                                                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                    int* __restrict__ recheck_count, int* __restrict__ recheck_list) {
   const int lane = threadIdx.x & 63;
@@ -275,8 +327,15 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, 
       key[j] = score[j] + ((bias && valid[j]) ? bias[e] : 0.f);
     }
   }
+  // gates above come from every expert; the group limit only narrows the selection
+  float ggap = __builtin_inff();
+  int n_allowed = E;
+  if (G > 0) {
+    ggap = group_limit_wave<float>(key, valid, E, G, M, lane);
+    n_allowed = M * (E / G);
+  }
   int my_e;
-  const float gap = wave_topk_f32(key, valid, E, K, lane, my_e);
+  const float gap = fminf(wave_topk_f32(key, valid, n_allowed, K, lane, my_e), ggap);
   // gate of this lane's expert: fetch score[my_e >> 6] from lane my_e & 63
   const int src = my_e < 0 ? 0 : (my_e & 63);
   float g = 0.f;
@@ -369,7 +428,7 @@ __global__ __launch_bounds__(kRecheckThreads) void router_recheck_logits(const T
 // Pass 2: one wave per flagged token selects again from the fp64 logits and rewrites its outputs.
 template <int GATE>
 __global__ __launch_bounds__(256) void router_recheck_select(const double* __restrict__ z64, int E, int K,
-                                                             const float* __restrict__ bias, int renorm,
+                                                             const float* __restrict__ bias, int renorm, int G, int M,
                                                              const int* __restrict__ recheck_count,
                                                              const int* __restrict__ recheck_list,
                                                              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
@@ -411,6 +470,7 @@ __global__ __launch_bounds__(256) void router_recheck_select(const double* __res
         key[j] = score[j] + ((bias && valid[j]) ? (double)bias[e] : 0.0);
       }
     }
+    if (G > 0) group_limit_wave<double>(key, valid, E, G, M, lane);
     // K rounds of (key descending, index ascending) argmax over 64-bit ordered keys
     uint64_t ok[4];
 #pragma unroll
@@ -491,10 +551,12 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   const int nb = cdiv(a.T, 4);
   if (a.gate == MOE_GATE_SOFTMAX)
-    router_topk<MOE_GATE_SOFTMAX><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.delta, a.topk_idx,
+    router_topk<MOE_GATE_SOFTMAX><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.n_groups, a.topk_groups,
+                                                     a.delta, a.topk_idx,
                                                      a.topk_w, a.recheck_count, a.recheck_list);
   else
-    router_topk<MOE_GATE_SIGMOID_BIAS><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.delta, a.topk_idx,
+    router_topk<MOE_GATE_SIGMOID_BIAS><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.n_groups,
+                                                          a.topk_groups, a.delta, a.topk_idx,
                                                           a.topk_w, a.recheck_count, a.recheck_list);
   if (a.u_bf16)
     router_recheck_logits<uint16_t><<<a.E, kRecheckThreads, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.E, a.d,
@@ -503,10 +565,12 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     router_recheck_logits<float><<<a.E, kRecheckThreads, 0, s>>>((const float*)a.u, a.wg, a.off, a.E, a.d,
                                                                   a.recheck_count, a.recheck_list, a.z64);
   if (a.gate == MOE_GATE_SOFTMAX)
-    router_recheck_select<MOE_GATE_SOFTMAX><<<64, 256, 0, s>>>(a.z64, a.E, a.K, a.bias, a.renorm, a.recheck_count,
+    router_recheck_select<MOE_GATE_SOFTMAX><<<64, 256, 0, s>>>(a.z64, a.E, a.K, a.bias, a.renorm, a.n_groups,
+                                                               a.topk_groups, a.recheck_count,
                                                                a.recheck_list, a.topk_idx, a.topk_w);
   else
-    router_recheck_select<MOE_GATE_SIGMOID_BIAS><<<64, 256, 0, s>>>(a.z64, a.E, a.K, a.bias, a.renorm,
+    router_recheck_select<MOE_GATE_SIGMOID_BIAS><<<64, 256, 0, s>>>(a.z64, a.E, a.K, a.bias, a.renorm, a.n_groups,
+                                                                    a.topk_groups,
                                                                     a.recheck_count, a.recheck_list, a.topk_idx,
                                                                     a.topk_w);
   return hipGetLastError();

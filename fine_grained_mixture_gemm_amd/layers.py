@@ -27,7 +27,7 @@ class DeviceLayer:
 def workload_config(w: configs.Workload):
     return make_config(w.T, w.d, w.E, w.Ks, w.K, w.f, MOE_GATE_SOFTMAX if w.gate == "softmax" else MOE_GATE_SIGMOID_BIAS,
                        w.renorm, MOE_F32 if w.act == "f32" else MOE_BF16,
-                       {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}[w.wdt])
+                       {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}[w.wdt], w.n_groups, w.topk_groups)
 
 
 def _fill_w13(dst, w, e, rows):

@@ -65,6 +65,14 @@ typedef struct {
   int32_t renorm;      /* 1: gates divided by their sum over the selected experts */
   int32_t act_dtype;   /* moe_dtype of u, h */
   int32_t w_dtype;     /* moe_dtype of expert weights */
+  /* Group-limited routing (DeepSeek Technical Report: MoE Architecture, 2.3 device-limited routing,
+   * M = 3 devices; 3.2 / 3.8 node-limited routing, M = 4 nodes). 0 / 0: no limit. Otherwise the E
+   * experts form n_groups equal contiguous groups (1..16, dividing E); a group scores the largest
+   * selection key among its experts; each token keeps the topk_groups best groups (ties to the lower
+   * group index) and takes its top-K among their experts (K <= topk_groups * E / n_groups). Gates are
+   * computed as without the limit. */
+  int32_t n_groups;
+  int32_t topk_groups;
 } moe_config;
 
 /* Layer weights (device pointers, read only).

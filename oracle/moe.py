@@ -214,7 +214,7 @@ def bias_update(bias, counts, gamma: float, T: int, K: int) -> np.ndarray:
 
 # ---------------------------------------------------------------------------------------- layer
 def layer_forward(u, w_gate, experts, shared, *, gate: str, K: int, bias=None, renorm=False,
-                  logit_offset=None, fp8=False):
+                  logit_offset=None, fp8=False, n_groups: int = 0, topk_groups: int = 0):
     """The whole layer. ``experts[e]`` and ``shared`` are the expert weights:
 
     float path: (w1 [f, d], w3 [f, d], w2 [d, f]) as stored (fp32 or bf16 values);
@@ -226,7 +226,7 @@ def layer_forward(u, w_gate, experts, shared, *, gate: str, K: int, bias=None, r
     T = u.shape[0]
     E = len(experts)
     z = router_logits(u, w_gate, logit_offset)
-    r = route(z, gate, K, bias, renorm)
+    r = route(z, gate, K, bias, renorm, n_groups, topk_groups)
     offsets, perm_src, row_of = dispatch(r["idx"], E)
     ffn = (lambda x, p: swiglu_ffn_fp8(x, *p)[0]) if fp8 else (lambda x, p: swiglu_ffn(x, *p))
     d = u.shape[1]

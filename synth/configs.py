@@ -46,6 +46,8 @@ class Workload:
     zipf: Optional[float] = None
     bias_range: Optional[float] = None
     gamma: Optional[float] = None   # bias update speed, when the workload includes one
+    n_groups: int = 0               # group-limited routing: experts in n_groups groups, topk_groups kept
+    topk_groups: int = 0
 
     @property
     def fs(self) -> int:

@@ -56,7 +56,8 @@ def make_cfg(w: configs.Workload) -> moe.moe_config:
     return moe.make_config(w.T, w.d, w.E, w.Ks, w.K, w.f,
                            moe.MOE_GATE_SOFTMAX if w.gate == "softmax" else moe.MOE_GATE_SIGMOID_BIAS, w.renorm,
                            moe.MOE_F32 if w.act == "f32" else moe.MOE_BF16,
-                           {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3}[w.wdt])
+                           {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3}[w.wdt],
+                           w.n_groups, w.topk_groups)
 
 
 def _store(x32: np.ndarray, wdt: str) -> tuple[torch.Tensor, np.ndarray]:

@@ -50,6 +50,12 @@ def _cfg(**kw):
     (dict(d_model=384), moe.MOE_ERR_UNSUPPORTED),          # bf16 / fp8 experts need d % 256 == 0
     (dict(inter_dim=100), moe.MOE_ERR_UNSUPPORTED),
     (dict(d_model=8448), moe.MOE_ERR_UNSUPPORTED),         # fp64 recheck holds d <= 8192
+    (dict(n_groups=3, topk_groups=1), moe.MOE_ERR_INVALID_ARG),    # 16 experts do not split into 3 groups
+    (dict(n_groups=4, topk_groups=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=4, topk_groups=5), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=0, topk_groups=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_groups=16, topk_groups=2), moe.MOE_ERR_INVALID_ARG),   # K = 4 > 2 groups x 1 expert
+    (dict(n_routed=64, n_groups=32, topk_groups=8), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_configs(kw, status):
     with pytest.raises(moe.MoeError) as e:
@@ -60,6 +66,7 @@ def test_invalid_configs(kw, status):
 
 def test_workspace_size_and_valid_configs():
     assert moe.moe_workspace_size(_cfg()) > 0
+    assert moe.moe_workspace_size(_cfg(n_groups=4, topk_groups=2)) > 0
     assert moe.moe_workspace_size(_cfg(T=0)) > 0
     assert moe.moe_workspace_size(_cfg(act_dtype=moe.MOE_F32, w_dtype=moe.MOE_F32, d_model=100, inter_dim=30)) > 0
     big = moe.moe_workspace_size(_cfg(T=8192, d_model=7168, n_routed=256, top_k=8, inter_dim=2048))

@@ -29,6 +29,11 @@ SMALL = {
     "fp8_decode_3tiles": W["v3_fp8"].replace(name="fp8_decode_3tiles", T=64, d=512, E=6, K=4),
     "fp8_decode_2shared": W["v3_fp8"].replace(name="fp8_decode_2shared", T=40, d=512, E=16, Ks=2, K=6),
     "fp8_decode_k_equals_e": W["v3_fp8"].replace(name="fp8_decode_k_equals_e", T=64, d=256, E=4, K=4),
+    # group-limited routing: 4 groups of 4 keeping 2 (softmax), 8 groups of 4 keeping 4 (sigmoid + bias)
+    "bf16_group_limited": W["dsmoe2b_bf16"].replace(name="bf16_group_limited", T=300, d=256, E=16, K=3, f=128,
+                                                     n_groups=4, topk_groups=2),
+    "fp8_node_limited": W["v3_fp8"].replace(name="fp8_node_limited", T=200, d=512, E=32, K=8, n_groups=8,
+                                            topk_groups=4),
     "f32_sigmoid_norenorm": W["tiny_f32"].replace(name="f32_sigmoid_norenorm", gate="sigmoid_bias", renorm=False,
                                                   bias_range=0.1, T=77, E=9, K=3),
 }
@@ -42,7 +47,8 @@ def _oracle_layer(g):
     else:
         experts, shared = g.host_experts, g.host_shared
     return omoe.layer_forward(g.u_host, g.wg, experts, shared, gate=w.gate, K=w.K, bias=g.bias, renorm=w.renorm,
-                              logit_offset=g.off, fp8=(w.wdt == "fp8"))
+                              logit_offset=g.off, fp8=(w.wdt == "fp8"), n_groups=w.n_groups,
+                              topk_groups=w.topk_groups)
 
 
 def _check_all(g, o, ref):

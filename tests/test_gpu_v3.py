@@ -47,7 +47,7 @@ def _run(w):
 
 def _check_routing(w, o, z32, u, wg, bias, off):
     z = omoe.router_logits(u, wg, off)
-    r = omoe.route(z, w.gate, w.K, bias, w.renorm)
+    r = omoe.route(z, w.gate, w.K, bias, w.renorm, w.n_groups, w.topk_groups)
     key32 = 1.0 / (1.0 + np.exp(-z32.astype(np.float64))) if w.gate == "sigmoid_bias" else z32
     key64 = r["key"] - (bias[None, :] if (w.gate == "sigmoid_bias" and bias is not None) else 0.0)
     kerr = float(np.abs(key32 - key64).max())
@@ -99,6 +99,18 @@ def test_v3_layer_full_size():
     e_exp = H.err(H.to_np(o["y_r"][a:b]), y_ref)
     print(f"expert {e}: {b - a} rows, err {e_exp:.4f}", flush=True)
     assert e_exp <= H.TOL["fp8"]
+
+
+def test_v3_node_limited_routing_full_size():
+    # the V3 limit of the MoE report (3.2, 3.8): each token's experts on at most 4 of 8 nodes
+    w = configs.WORKLOADS["v3_fp8"].replace(name="v3_fp8_node_limited", n_groups=8, topk_groups=4)
+    print("[case] v3_fp8 node-limited routing", flush=True)
+    L, o, z32 = _run(w)
+    u, wg, bias, off = _host_inputs(w)
+    r, offsets, perm, row_of = _check_routing(w, o, z32, u, wg, bias, off)
+    groups = H.to_np(o["idx"]) // (w.E // w.n_groups)
+    assert max(len(set(row)) for row in groups.tolist()) <= w.topk_groups
+    _check_token0(w, o, u, r, row_of)
 
 
 def test_v3_decode_step_and_bias_update():
