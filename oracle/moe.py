@@ -184,6 +184,45 @@ def swiglu_ffn_fp8(x, w13q, w13s, w2q, w2s) -> tuple[np.ndarray, np.ndarray]:
     return y, a
 
 
+# ------------------------------------------------------------------------- expert backward (input)
+def swiglu_backward(da, g, v):
+    """Gradients of a = SiLU(g) * v with respect to g and v for the upstream gradient da (float64):
+    dv = da * SiLU(g), dg = da * v * SiLU'(g), SiLU'(g) = sigmoid(g) * (1 + g * (1 - sigmoid(g)))."""
+    da, g, v = (np.asarray(t, dtype=np.float64) for t in (da, g, v))
+    sig = sigmoid(g)
+    return da * v * sig * (1.0 + g * (1.0 - sig)), da * g * sig
+
+
+def swiglu_ffn_backward_input(dy, x, w1, w3, w2) -> np.ndarray:
+    """dx of FFN(x) = W2 (SiLU(W1 x) * (W3 x)) for the row gradients dy, float64 (the chain rule through
+    the three Linears and SwiGLU; [PW] "invariant core" for the FFN)."""
+    x = np.asarray(x, dtype=np.float64)
+    w1, w3, w2 = (np.asarray(w, dtype=np.float64) for w in (w1, w3, w2))
+    g, v = x @ w1.T, x @ w3.T
+    dg, dv = swiglu_backward(np.asarray(dy, dtype=np.float64) @ w2, g, v)
+    return dg @ w1 + dv @ w3
+
+
+def swiglu_ffn_backward_input_fp8(dy, x, w13q, w13s, w2q, w2s) -> np.ndarray:
+    """The activation backward GEMMs of the SwiGLU expert in E4M3 ([TR] §3.6: "activation backward
+    GEMM" in FP8, 1x128 activation tiles, 128x128 weight blocks, promotion every 128).
+
+    Readings (the pages fix the formats, not the dataflow): the cached forward input x is quantized
+    1x128 as in the forward and g, v are recomputed from it with the forward GEMM; the output gradient
+    dy is quantized 1x128 along d, the contraction of da = dy W2; the SwiGLU backward is evaluated and
+    rounded to fp32; [dg | dv] is quantized 1x128 along 2f, the contraction of dx = [dg | dv] [W1; W3].
+    A transposed weight keeps its E4M3 codes and the transposed grid of 128x128 block scales.
+    """
+    f = w13q.shape[0] // 2
+    xq, xs = quant.quantize_act_1x128(x)
+    gv = quant.gemm_blockscaled(xq, xs, w13q, w13s)
+    dyq, dys = quant.quantize_act_1x128(np.asarray(dy).astype(np.float32))
+    da = quant.gemm_blockscaled(dyq, dys, np.ascontiguousarray(w2q.T), np.ascontiguousarray(w2s.T))
+    dg, dv = swiglu_backward(da, gv[:, :f], gv[:, f:])
+    dgvq, dgvs = quant.quantize_act_1x128(np.hstack([dg, dv]).astype(np.float32))
+    return quant.gemm_blockscaled(dgvq, dgvs, np.ascontiguousarray(w13q.T), np.ascontiguousarray(w13s.T))
+
+
 # -------------------------------------------------------------------------------------- combine
 def combine(u, y_shared, y_rows, row_of, w) -> np.ndarray:
     """h_t = u_t + sum_shared FFN(u_t) + sum_k g_{k,t} FFN_{e_k}(u_t) ([TR] §1.1, §5.3 [1]).
