@@ -16,6 +16,7 @@ __all__ = [
     "moe_config", "moe_layer", "make_config", "make_layer", "moe_workspace_size", "moe_route", "moe_router_logits", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_forward", "moe_update_bias", "moe_quantize_weights",
     "moe_quantize_act", "moe_last_error", "moe_set_timing_events", "MOE_NUM_MARKS", "MARK_NAMES", "LIB_PATH",
+    "moe_balance_stats", "moe_backward_workspace_size", "moe_expert_ffn_backward_input", "moe_transpose_fp8_weights",
 ]
 
 # MOE_LIBRARY_PATH overrides the in-tree library (a developer switch for comparing builds).
@@ -61,6 +62,9 @@ _SIGS = {
     "moe_forward": [_CP, _LP, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_update_bias": [_CP, _vp, _f32, _vp, _vp],
     "moe_balance_stats": [_CP, _vp, _vp, _i32, _f32, _f32, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_backward_workspace_size": [_CP, ctypes.POINTER(_sz)],
+    "moe_expert_ffn_backward_input": [_CP, _LP, _LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_transpose_fp8_weights": [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp],
     "moe_quantize_weights": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
     "moe_quantize_act": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
     "moe_set_timing_events": [_vp, _i32],
@@ -156,6 +160,27 @@ def moe_update_bias(cfg, counts, gamma, bias, stream=None):
 def moe_balance_stats(cfg, z, topk_idx, seq_len, alpha_expert, alpha_seq, f, P, loss, ws, stream=None):
     _call("moe_balance_stats", ctypes.byref(cfg), _dev(z), _dev(topk_idx), int(seq_len), float(alpha_expert),
           float(alpha_seq), _dev(f), _dev(P), _dev(loss), _dev(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+          _stream(stream))
+
+
+def moe_backward_workspace_size(cfg) -> int:
+    n = _sz(0)
+    _call("moe_backward_workspace_size", ctypes.byref(cfg), ctypes.byref(n))
+    return n.value
+
+
+def moe_expert_ffn_backward_input(cfg, layer, layer_t, u, offsets, perm_src, dy_routed, dy_shared, dx_routed,
+                                  dx_shared, ws, stream=None):
+    _call("moe_expert_ffn_backward_input", ctypes.byref(cfg), ctypes.byref(layer), ctypes.byref(layer_t), _dev(u),
+          _dev(offsets), _dev(perm_src), _dev(dy_routed), _dev(dy_shared), _dev(dx_routed), _dev(dx_shared), _dev(ws),
+          ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+
+
+def moe_transpose_fp8_weights(q, scales, qt, scales_t, stream=None):
+    """q [batch, rows, cols] uint8 (or [rows, cols]), scales [batch, rows/128, cols/128] -> transposed copies."""
+    batch = q.shape[0] if q.dim() == 3 else 1
+    rows, cols = q.shape[-2], q.shape[-1]
+    _call("moe_transpose_fp8_weights", _dev(q), _dev(scales), batch, rows, cols, _dev(qt), _dev(scales_t),
           _stream(stream))
 
 

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["capi.hip", "router.hip", "dispatch.hip", "quant.hip", "gemm_mfma.hip", "gemm_decode.hip", "gemm_simt.hip", "combine.hip", "balance.hip"]
+SOURCES = ["capi.hip", "router.hip", "dispatch.hip", "quant.hip", "gemm_mfma.hip", "gemm_decode.hip", "gemm_simt.hip", "combine.hip", "balance.hip", "backward.hip"]
 LIB = os.path.join(PKG, "libmoe.so")
 SYNTH_SRC = os.path.join(ROOT, "synth", "csrc", "synth_dev.hip")
 SYNTH_LIB = os.path.join(ROOT, "synth", "libmoe_synth.so")

@@ -179,6 +179,53 @@ int device_cus() {
   return cached_cus;
 }
 
+// Workspace of the E4M3 input backward of the experts (its own size query).
+struct BwdLayout {
+  size_t uq, us, mt_prefix, xsched_a, xsched_b;
+  size_t dyq_r, dys_r, dyq_s, dys_s, da_r, da_s, gv_r, gv_s, dgq_r, dgs_r, dgq_s, dgs_s;
+  size_t total;
+};
+
+BwdLayout bwd_layout(const moe_config* c) {
+  BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  const size_t T = c->T, E = c->n_routed, d = c->d_model, f = c->inter_dim, fs = (size_t)c->n_shared * f;
+  const size_t rows = T * c->top_k;
+  L.uq = take(T * d);
+  L.us = take(T * (d / 128) * 4);
+  L.mt_prefix = take((E + 1) * 4);
+  L.xsched_a = take(2 * 9 * 4 + 2 * 8 * 4);
+  L.xsched_b = take(2 * 9 * 4 + 2 * 8 * 4);
+  L.dyq_r = take(rows * d);
+  L.dys_r = take(rows * (d / 128) * 4);
+  L.dyq_s = take(T * d * (fs > 0));
+  L.dys_s = take(T * (d / 128) * 4 * (fs > 0));
+  L.da_r = take(rows * f * 4);
+  L.da_s = take(T * fs * 4);
+  L.gv_r = take(rows * 2 * f * 4);
+  L.gv_s = take(T * 2 * fs * 4);
+  L.dgq_r = take(rows * 2 * f);
+  L.dgs_r = take(rows * (2 * f / 128) * 4);
+  L.dgq_s = take(T * 2 * fs);
+  L.dgs_s = take(T * (2 * fs / 128) * 4);
+  L.total = off + 256;
+  return L;
+}
+
+moe_status check_bwd_cfg(const moe_config* c) {
+  MOE_TRY(check_cfg(c));
+  if (c->w_dtype != MOE_FP8_E4M3) return fail(MOE_ERR_UNSUPPORTED, "the expert input backward is built for E4M3 experts");
+  if (c->n_shared > 1) return fail(MOE_ERR_UNSUPPORTED, "the expert input backward takes at most one shared expert");
+  if (c->inter_dim % 256) return fail(MOE_ERR_UNSUPPORTED, "the expert input backward needs inter_dim %% 256 == 0");
+  if (2 * c->inter_dim > 8192) return fail(MOE_ERR_UNSUPPORTED, "the expert input backward needs 2 * inter_dim <= 8192");
+  return MOE_OK;
+}
+
 moe_status check_layer_router(const moe_layer* l) {
   if (!l) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
   if (!l->w_gate) return fail(MOE_ERR_INVALID_ARG, "layer->w_gate is NULL");
@@ -509,6 +556,122 @@ moe_status moe_balance_stats(const moe_config* cfg, const float* z, const int32_
   a.P = P;
   a.loss = loss;
   return hip_status(launch_balance_stats(a, stream), "balance statistics launch");
+}
+
+moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes) {
+  MOE_TRY(check_bwd_cfg(cfg));
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = bwd_layout(cfg).total;
+  return MOE_OK;
+}
+
+moe_status moe_transpose_fp8_weights(const uint8_t* q, const float* scales, int32_t batch, int32_t rows, int32_t cols,
+                                     uint8_t* qt, float* scales_t, hipStream_t stream) {
+  if (batch < 0 || rows <= 0 || cols <= 0) return fail(MOE_ERR_INVALID_ARG, "bad sizes batch=%d rows=%d cols=%d", batch, rows, cols);
+  if (rows % 128 || cols % 128) return fail(MOE_ERR_UNSUPPORTED, "rows and cols must be multiples of 128");
+  if (batch > 65535 || rows / 64 > 65535) return fail(MOE_ERR_UNSUPPORTED, "too many blocks");
+  if (batch > 0 && (!q || !scales || !qt || !scales_t)) return fail(MOE_ERR_INVALID_ARG, "q / scales / qt / scales_t is NULL");
+  return hip_status(launch_transpose_fp8(q, scales, batch, rows, cols, qt, scales_t, stream), "weight transpose launch");
+}
+
+moe_status moe_expert_ffn_backward_input(const moe_config* cfg, const moe_layer* layer, const moe_layer* layer_t,
+                                         const void* u, const int32_t* offsets, const int32_t* perm_src,
+                                         const void* dy_routed, const void* dy_shared, void* dx_routed, void* dx_shared,
+                                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_bwd_cfg(cfg));
+  MOE_TRY(check_layer_experts(cfg, layer));
+  MOE_TRY(check_layer_experts(cfg, layer_t));
+  const moe_config* c = cfg;
+  const bool sh = c->n_shared > 0;
+  if (c->T > 0 && (!u || !offsets || !perm_src || !dy_routed || !dx_routed))
+    return fail(MOE_ERR_INVALID_ARG, "u / offsets / perm_src / dy_routed / dx_routed is NULL");
+  if (c->T > 0 && sh && (!dy_shared || !dx_shared)) return fail(MOE_ERR_INVALID_ARG, "dy_shared / dx_shared is NULL with n_shared > 0");
+  const BwdLayout L = bwd_layout(c);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
+  if (c->T == 0) return MOE_OK;
+  uint8_t* base = reinterpret_cast<uint8_t*>(align_up(reinterpret_cast<uintptr_t>(ws), 256));
+  hipStream_t s = stream;
+  const int T = c->T, E = c->n_routed, d = c->d_model, f = c->inter_dim, fs = c->n_shared * f;
+  const int rows = T * c->top_k;
+  const int bm = gemm_mfma_bm(), grid = device_cus() / 8 * 8;
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(base + o); };
+  int32_t* mt_prefix = reinterpret_cast<int32_t*>(base + L.mt_prefix);
+  int32_t* xa = reinterpret_cast<int32_t*>(base + L.xsched_a);
+  int32_t* xb = reinterpret_cast<int32_t*>(base + L.xsched_b);
+  // tile ranges: (g, v) recompute [gate/up shape] and da = dy W2 [down shape, output f]; then dx [output d]
+  {
+    const int nt_r[2] = {f / 128, f / 256}, nt_s[2] = {fs / 128, sh ? f / 256 : 0};
+    MOE_TRY(hip_status(launch_schedule_mfma(offsets, E, T, bm, nt_r, nt_s, mt_prefix, xa, xa + 18, s), "schedule launch"));
+    const int nt_r2[2] = {f / 128, d / 256}, nt_s2[2] = {0, sh ? d / 256 : 0};
+    MOE_TRY(hip_status(launch_schedule_mfma(offsets, E, T, bm, nt_r2, nt_s2, mt_prefix, xb, xb + 18, s), "schedule launch"));
+  }
+  // cached forward input: u quantized 1x128 as in the forward
+  MOE_TRY(hip_status(launch_quant_act(u, true, T, d, base + L.uq, F(L.us), s), "activation quantization launch"));
+  GemmArgs g{};
+  g.E = E;
+  g.T = T;
+  g.offsets = offsets;
+  g.perm_src = perm_src;
+  g.mt_prefix = mt_prefix;
+  // 1. [g | v] = x [W1; W3]^T in fp32 (the forward's gate/up GEMM without SwiGLU)
+  g.d = d;
+  g.f = f;
+  g.fs = fs;
+  g.xrange = xa;
+  g.xcount = xa + 18;
+  g.w_routed = static_cast<const uint8_t*>(layer->w13);
+  g.w_shared = static_cast<const uint8_t*>(layer->ws13);
+  g.ws_routed = layer->w13_scale;
+  g.ws_shared = layer->ws13_scale;
+  g.x_routed = g.x_shared = base + L.uq;
+  g.xs_routed = g.xs_shared = F(L.us);
+  g.out_routed = base + L.gv_r;
+  g.out_shared = base + L.gv_s;
+  MOE_TRY(hip_status(launch_gemm_mfma(g, true, true, grid, s, true), "g/v GEMM launch"));
+  // 2. dy quantized 1x128 along d; da = dy W2 (weights W2^T [f, d]: output f, contraction d), fp32
+  MOE_TRY(hip_status(launch_quant_act(dy_routed, true, rows, d, base + L.dyq_r, F(L.dys_r), s), "dy quantization launch"));
+  if (sh) MOE_TRY(hip_status(launch_quant_act(dy_shared, true, T, d, base + L.dyq_s, F(L.dys_s), s), "dy quantization launch"));
+  g.d = f;
+  g.f = d;
+  g.fs = d;
+  g.xrange = xa + 9;
+  g.xcount = xa + 18 + 8;
+  g.w_routed = static_cast<const uint8_t*>(layer_t->w2);
+  g.w_shared = static_cast<const uint8_t*>(layer_t->ws2);
+  g.ws_routed = layer_t->w2_scale;
+  g.ws_shared = layer_t->ws2_scale;
+  g.x_routed = base + L.dyq_r;
+  g.x_shared = base + L.dyq_s;
+  g.xs_routed = F(L.dys_r);
+  g.xs_shared = F(L.dys_s);
+  g.out_routed = base + L.da_r;
+  g.out_shared = base + L.da_s;
+  MOE_TRY(hip_status(launch_gemm_mfma(g, true, false, grid, s, true), "da GEMM launch"));
+  // 3. [dg | dv] from da, g, v, quantized 1x128 along 2f
+  MOE_TRY(hip_status(launch_swiglu_backward_quant(F(L.da_r), F(L.gv_r), rows, f, base + L.dgq_r, F(L.dgs_r), s),
+                     "SwiGLU backward launch"));
+  if (sh)
+    MOE_TRY(hip_status(launch_swiglu_backward_quant(F(L.da_s), F(L.gv_s), T, fs, base + L.dgq_s, F(L.dgs_s), s),
+                       "SwiGLU backward launch"));
+  // 4. dx = [dg | dv] [W1; W3] (weights [W1; W3]^T [d, 2f]: output d, contraction 2f), bf16
+  g.d = d;
+  g.f = 2 * f;
+  g.fs = 2 * fs;
+  g.xrange = xb + 9;
+  g.xcount = xb + 18 + 8;
+  g.w_routed = static_cast<const uint8_t*>(layer_t->w13);
+  g.w_shared = static_cast<const uint8_t*>(layer_t->ws13);
+  g.ws_routed = layer_t->w13_scale;
+  g.ws_shared = layer_t->ws13_scale;
+  g.x_routed = base + L.dgq_r;
+  g.x_shared = base + L.dgq_s;
+  g.xs_routed = F(L.dgs_r);
+  g.xs_shared = F(L.dgs_s);
+  g.out_routed = static_cast<uint8_t*>(dx_routed);
+  g.out_shared = static_cast<uint8_t*>(dx_shared);
+  MOE_TRY(hip_status(launch_gemm_mfma(g, true, false, grid, s, false), "dx GEMM launch"));
+  return MOE_OK;
 }
 
 moe_status moe_quantize_weights(const float* w, int32_t batch, int32_t rows, int32_t cols, uint8_t* q, float* scales,

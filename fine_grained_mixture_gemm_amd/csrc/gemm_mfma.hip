@@ -193,7 +193,9 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[4][kTJ], const uint8_t* _
   }
 }
 
-template <bool FP8, bool GATEUP>
+// RAW: the accumulators are stored in fp32 as they are (gate/up: g and v, no SwiGLU; down: fp32 instead
+// of bf16), for the input backward of the experts.
+template <bool FP8, bool GATEUP, bool RAW = false>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -360,7 +362,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
     // weight tile i (gate/up: gate channels 32 wn + 16 i for i < 2, their up channels for i >= 2).
     const bool shared = tc.group == E;
     const int fg = shared ? a.fs : a.f;
-    if constexpr (GATEUP) {
+    if constexpr (GATEUP && RAW) {
+      // [g | v] in fp32, row stride 2 fg: gate channel c at column c, its up channel at fg + c
+      const int c0 = tc.n_tile * 128;
+      const size_t ostride = (size_t)2 * fg;
+      float* OUTF = reinterpret_cast<float*>(shared ? a.out_shared : a.out_routed) + (size_t)tc.rowbase * ostride +
+                    c0 + 32 * wn + 4 * g;
+#pragma unroll
+      for (int j = 0; j < kTJ; ++j) {
+        const int tok = tok0 + 16 * j + tr;
+        if (tok < tc.nrows) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<f32x4*>(OUTF + (size_t)tok * ostride + 16 * (i & 1) + (i >= 2 ? fg : 0)) = acc[i][j];
+        }
+      }
+    } else if constexpr (GATEUP) {
       const int c0 = tc.n_tile * 128;
       float av[2][kTJ][4];
 #pragma unroll
@@ -420,7 +437,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
       }
     } else {
       const int c0 = tc.n_tile * kBW;
-      constexpr int ysz = FP8 ? 2 : 4;   // y in bf16 (the combine payload of the E4M3 path) or fp32
+      constexpr int ysz = (FP8 && !RAW) ? 2 : 4;   // y in bf16 (the combine payload of the E4M3 path) or fp32
       const size_t out_stride = (size_t)a.d * ysz;
       uint8_t* OUT = (shared ? a.out_shared : a.out_routed) + (size_t)tc.rowbase * out_stride +
                      (size_t)(c0 + 64 * wn + 4 * g) * ysz;
@@ -431,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             uint8_t* o = OUT + (size_t)tok * out_stride + 16 * i * ysz;
-            if constexpr (FP8) {
+            if constexpr (FP8 && !RAW) {
               uint2 v;
               v.x = uint32_t(f32_to_bf16(acc[i][j][0])) | (uint32_t(f32_to_bf16(acc[i][j][1])) << 16);
               v.y = uint32_t(f32_to_bf16(acc[i][j][2])) | (uint32_t(f32_to_bf16(acc[i][j][3])) << 16);
@@ -459,22 +476,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
 
 int gemm_mfma_bm() { return kBM; }
 
-hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s) {
-  static bool attr_done[4] = {false, false, false, false};
-  const int k = (fp8 ? 2 : 0) + (gateup ? 1 : 0);
-  const void* fn = fp8 ? (gateup ? (const void*)grouped_gemm_mfma<true, true> : (const void*)grouped_gemm_mfma<true, false>)
-                       : (gateup ? (const void*)grouped_gemm_mfma<false, true> : (const void*)grouped_gemm_mfma<false, false>);
+hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s, bool raw) {
+  if (raw && !fp8) return hipErrorInvalidValue;
+  static bool attr_done[6] = {false, false, false, false, false, false};
+  const int k = raw ? 4 + (gateup ? 1 : 0) : (fp8 ? 2 : 0) + (gateup ? 1 : 0);
+  const void* fns[6] = {(const void*)grouped_gemm_mfma<false, false>, (const void*)grouped_gemm_mfma<false, true>,
+                        (const void*)grouped_gemm_mfma<true, false>, (const void*)grouped_gemm_mfma<true, true>,
+                        (const void*)grouped_gemm_mfma<true, false, true>, (const void*)grouped_gemm_mfma<true, true, true>};
   if (!attr_done[k]) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    hipError_t e = hipFuncSetAttribute(fns[k], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_done[k] = true;
   }
-  if (fp8) {
-    if (gateup) grouped_gemm_mfma<true, true><<<grid, kThreads, kLdsBytes, s>>>(a);
-    else grouped_gemm_mfma<true, false><<<grid, kThreads, kLdsBytes, s>>>(a);
-  } else {
-    if (gateup) grouped_gemm_mfma<false, true><<<grid, kThreads, kLdsBytes, s>>>(a);
-    else grouped_gemm_mfma<false, false><<<grid, kThreads, kLdsBytes, s>>>(a);
+  switch (k) {
+    case 0: grouped_gemm_mfma<false, false><<<grid, kThreads, kLdsBytes, s>>>(a); break;
+    case 1: grouped_gemm_mfma<false, true><<<grid, kThreads, kLdsBytes, s>>>(a); break;
+    case 2: grouped_gemm_mfma<true, false><<<grid, kThreads, kLdsBytes, s>>>(a); break;
+    case 3: grouped_gemm_mfma<true, true><<<grid, kThreads, kLdsBytes, s>>>(a); break;
+    case 4: grouped_gemm_mfma<true, false, true><<<grid, kThreads, kLdsBytes, s>>>(a); break;
+    default: grouped_gemm_mfma<true, true, true><<<grid, kThreads, kLdsBytes, s>>>(a); break;
   }
   return hipGetLastError();
 }

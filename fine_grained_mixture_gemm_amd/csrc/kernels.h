@@ -106,7 +106,12 @@ hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_pr
 hipError_t launch_schedule_mfma(const int32_t* offsets, int E, int T, int bm, const int (&nt_r)[2], const int (&nt_s)[2],
                                 int32_t* mt_prefix, int32_t* xrange, int32_t* xcount, hipStream_t s);
 int gemm_mfma_bm();
-hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s);
+// raw (E4M3 only): fp32 accumulators out (gate/up: g and v without SwiGLU; down: fp32 instead of bf16)
+hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s, bool raw = false);
+hipError_t launch_swiglu_backward_quant(const float* da, const float* gv, int rows, int fg, uint8_t* q, float* scales,
+                                        hipStream_t s);
+hipError_t launch_transpose_fp8(const uint8_t* q, const float* scales, int batch, int rows, int cols, uint8_t* qt,
+                                float* scales_t, hipStream_t s);
 int balance_chunks_for(int T);
 int balance_sequences_max(int T);   // sequences of T tokens when seq_len is T or a multiple of 64
 hipError_t launch_balance_stats(const BalanceArgs& a, hipStream_t s);

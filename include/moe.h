@@ -160,6 +160,37 @@ moe_status moe_forward(const moe_config* cfg, const moe_layer* layer, const void
 moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* bias,
                            hipStream_t stream);
 
+/* Input backward of the E4M3 experts (DeepSeek Technical Report: MoE Architecture, 3.6: the
+ * activation backward GEMMs in FP8 with 1x128 activation tiles, 128x128 weight blocks and fp32
+ * promotion every 128 elements). For every routed row r (dispatch order, as moe_expert_ffn's y_routed)
+ * and every token of the shared block, given dy = dL/dy of the expert output, computes
+ * dx = dL/dx of the expert input x (the token's u):
+ *   g, v  = x [W1; W3]^T, recomputed in fp32 from x quantized 1x128 exactly as in the forward;
+ *   da    = dy W2, with dy quantized 1x128 along d;
+ *   dg    = da * v * sigmoid(g) * (1 + g (1 - sigmoid(g))),  dv = da * SiLU(g)   (fp32);
+ *   dx    = [dg | dv] [W1; W3], with [dg | dv] quantized 1x128 along 2f.
+ *  cfg      E4M3 experts (w_dtype MOE_FP8_E4M3), n_shared 0 or 1, inter_dim % 256 == 0 and
+ *           2 * inter_dim <= 8192 (else MOE_ERR_UNSUPPORTED).
+ *  layer    the forward weights (w13, w13_scale, ws13, ws13_scale are used).
+ *  layer_t  the same weights transposed (moe_transpose_fp8_weights): w13 = [W1; W3]^T [E, d, 2f] with
+ *           scales [E, d/128, 2f/128], w2 = W2^T [E, f, d] with scales [E, f/128, d/128]; ws13 / ws2
+ *           likewise for the shared block.
+ *  u [T, d] bf16 (the layer input), offsets / perm_src as moe_dispatch returns them.
+ *  dy_routed [T*K, d] bf16, dy_shared [T, d] bf16 (n_shared == 1); dx_routed [T*K, d] bf16 out,
+ *  dx_shared [T, d] bf16 out.
+ *  ws / ws_bytes: a workspace of at least moe_backward_workspace_size bytes. */
+moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
+moe_status moe_expert_ffn_backward_input(const moe_config* cfg, const moe_layer* layer, const moe_layer* layer_t,
+                                         const void* u, const int32_t* offsets, const int32_t* perm_src,
+                                         const void* dy_routed, const void* dy_shared, void* dx_routed,
+                                         void* dx_shared, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Transpose a batch of E4M3 matrices with their 128x128 block scales: qt[m] = q[m]^T ([cols, rows]),
+ * scales_t[m] = scales[m]^T ([cols/128, rows/128]); the codes are unchanged, so a transposed block keeps
+ * its scale. rows and cols are multiples of 128. Device pointers; qt must not alias q. */
+moe_status moe_transpose_fp8_weights(const uint8_t* q, const float* scales, int32_t batch, int32_t rows, int32_t cols,
+                                     uint8_t* qt, float* scales_t, hipStream_t stream);
+
 /* Load-balance statistics of one routed batch (DeepSeek Technical Report: MoE Architecture, 1.2
  * expert-level balance loss L_ExpBal = alpha_1 * sum_i f_i * P_i, alpha_1 = 0.003 in 2.3; 3.3 the V3
  * sequence-wise balance loss, weight 0.0001, formula not printed). Readings: f_i = (tokens whose top-K

@@ -123,3 +123,34 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         moe.moe_quantize_act(torch.zeros(4, 128), moe.MOE_F32, torch.zeros(4, 128, dtype=torch.uint8), torch.zeros(4, 1))
+
+
+def test_backward_argument_errors():
+    # every check runs before any launch: non-null dummy pointers are never dereferenced
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_backward_workspace_size(_cfg(act_dtype=moe.MOE_BF16, w_dtype=moe.MOE_BF16))
+    assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_backward_workspace_size(_cfg(n_shared=2))
+    assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_backward_workspace_size(_cfg(inter_dim=128))      # da tiles are 256 channels wide
+    assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+    cfg = _cfg(inter_dim=256)
+    need = moe.moe_backward_workspace_size(cfg)
+    assert need > 64 * 4 * 2 * 256 * 4          # at least the fp32 [g | v] of the routed rows
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    P = ctypes.POINTER
+    lib.moe_expert_ffn_backward_input.argtypes = ([P(moe.moe_config), P(moe.moe_layer), P(moe.moe_layer)] +
+                                                  [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p])
+    full = moe.moe_layer(16, 16, 16, 16, 16, 16, 16, 16, 16, None)
+    call = lambda lt=full, dys=16, ws=16, nbytes=need: lib.moe_expert_ffn_backward_input(
+        ctypes.byref(cfg), ctypes.byref(full), ctypes.byref(lt), 16, 16, 16, 16, dys, 16, 16, ws, nbytes, None)
+    assert call(lt=moe.moe_layer()) == moe.MOE_ERR_INVALID_ARG           # transposed weights missing
+    assert call(dys=None) == moe.MOE_ERR_INVALID_ARG                      # shared gradient missing
+    assert call(nbytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(ws=None) == moe.MOE_ERR_WORKSPACE
+    lib.moe_transpose_fp8_weights.argtypes = [ctypes.c_void_p, ctypes.c_void_p] + [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 3
+    assert lib.moe_transpose_fp8_weights(16, 16, 1, 192, 128, 16, 16, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_transpose_fp8_weights(16, 16, -1, 128, 128, 16, 16, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_transpose_fp8_weights(None, 16, 1, 128, 128, 16, 16, None) == moe.MOE_ERR_INVALID_ARG
