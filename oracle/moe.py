@@ -223,6 +223,46 @@ def swiglu_ffn_backward_input_fp8(dy, x, w13q, w13s, w2q, w2s) -> np.ndarray:
     return quant.gemm_blockscaled(dgvq, dgvs, np.ascontiguousarray(w13q.T), np.ascontiguousarray(w13s.T))
 
 
+# ------------------------------------------------------------------------ expert backward (weights)
+def swiglu_ffn_backward_weight(dy, x, w1, w3, w2):
+    """(dW1, dW3, dW2) of FFN(x) = W2 (SiLU(W1 x) * (W3 x)) summed over the rows of x for the row
+    gradients dy, float64: dW2 = dy^T a with a = SiLU(g) * v, dW1 = dg^T x, dW3 = dv^T x."""
+    x, dy = np.asarray(x, dtype=np.float64), np.asarray(dy, dtype=np.float64)
+    w1, w3, w2 = (np.asarray(w, dtype=np.float64) for w in (w1, w3, w2))
+    g, v = x @ w1.T, x @ w3.T
+    dg, dv = swiglu_backward(dy @ w2, g, v)
+    return dg.T @ x, dv.T @ x, dy.T @ (silu(g) * v)
+
+
+def swiglu_ffn_backward_weight_fp8(dy, x, w13q, w13s, w2q, w2s):
+    """The weight-gradient GEMMs of the SwiGLU expert in E4M3 ([TR] §3.6: the weight backward GEMM runs
+    in FP8, activations cached for the backward are FP8, weight gradients are kept in BF16).
+
+    Readings: the contraction of dW2 = dy^T a and of d[W1; W3] = [dg | dv]^T x is over the rows
+    (tokens), so both operands are quantized in 1x128 tiles along the rows (quant.quantize_act_along_rows;
+    an expert's last tile is padded with zero rows). The cached activations enter as the values their
+    forward E4M3 copies hold: x as its 1x128 quantization along d, a = SiLU(g) * v as its 1x128
+    requantization along f, each dequantized (rounded to fp32) and requantized along the rows. dy enters
+    as given, [dg | dv] as its fp32 value from the input backward (swiglu_ffn_backward_input_fp8).
+    Returns (dW13 [2f, d] with the W1 rows first, dW2 [d, f]) in float64, before the BF16 rounding.
+    """
+    f = w13q.shape[0] // 2
+    xq, xs = quant.quantize_act_1x128(x)
+    gv = quant.gemm_blockscaled(xq, xs, w13q, w13s)
+    g, v = gv[:, :f], gv[:, f:]
+    aq, as_ = quant.quantize_act_1x128((silu(g) * v).astype(np.float32))
+    dy32 = np.asarray(dy).astype(np.float32)
+    dyq, dys = quant.quantize_act_1x128(dy32)
+    da = quant.gemm_blockscaled(dyq, dys, np.ascontiguousarray(w2q.T), np.ascontiguousarray(w2s.T))
+    dg, dv = swiglu_backward(da, g, v)
+    dgv = np.hstack([dg, dv]).astype(np.float32)
+    dw2 = quant.gemm_rowscaled(*quant.quantize_act_along_rows(dy32),
+                               *quant.quantize_act_along_rows(quant.dequant_act(aq, as_)))
+    dw13 = quant.gemm_rowscaled(*quant.quantize_act_along_rows(dgv),
+                                *quant.quantize_act_along_rows(quant.dequant_act(xq, xs)))
+    return dw13, dw2
+
+
 # -------------------------------------------------------------------------------------- combine
 def combine(u, y_shared, y_rows, row_of, w) -> np.ndarray:
     """h_t = u_t + sum_shared FFN(u_t) + sum_k g_{k,t} FFN_{e_k}(u_t) ([TR] §1.1, §5.3 [1]).

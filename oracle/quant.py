@@ -90,3 +90,35 @@ def gemm_blockscaled(xq, xs, wq, ws) -> np.ndarray:
         sw = np.repeat(ws[:, kb].astype(np.float64), TILE)[None, :]
         out += (xs[:, kb].astype(np.float64)[:, None] * sw) * p
     return out
+
+
+def quantize_act_along_rows(x) -> tuple[np.ndarray, np.ndarray]:
+    """1x128 tiles that run down the columns: the operand of a GEMM whose contraction is over the rows
+    (the weight-gradient GEMMs, where the contraction is over tokens).
+
+    x [rows, cols] (cols % 128 == 0) is padded with zero rows to a multiple of 128 and every column is
+    quantized in blocks of 128 consecutive rows with the rule above. Returns the codes transposed, so the
+    contraction runs along the last axis: (codes uint8 [cols, rows_pad], scales fp32 [cols, rows_pad/128]).
+    """
+    x32 = np.asarray(x).astype(np.float32)
+    rows, cols = x32.shape
+    pad = -rows % TILE
+    xp = np.vstack([x32, np.zeros((pad, cols), dtype=np.float32)])
+    return quantize_act_1x128(np.ascontiguousarray(xp.T))
+
+
+def gemm_rowscaled(aq, as_, bq, bs) -> np.ndarray:
+    """out[m, n] = sum_kb as_[m, kb] * bs[n, kb] * sum_{k in block kb} q_a[m, k] q_b[n, k].
+
+    Both operands carry one scale per row per 128 contraction elements (quantize_act_along_rows), so each
+    128-term partial sum is promoted with the product of its two tile scales ([TR] §3.6 promotion every
+    128 elements). float64; the inner sums are exact as in gemm_blockscaled.
+    """
+    av = e4m3_decode(aq)
+    bv = e4m3_decode(bq)
+    m, k = av.shape
+    out = np.zeros((m, bv.shape[0]), dtype=np.float64)
+    for kb in range(k // TILE):
+        sl = slice(kb * TILE, (kb + 1) * TILE)
+        out += (as_[:, kb].astype(np.float64)[:, None] * bs[:, kb].astype(np.float64)[None, :]) * (av[:, sl] @ bv[:, sl].T)
+    return out
