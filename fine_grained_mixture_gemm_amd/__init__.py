@@ -17,6 +17,7 @@ __all__ = [
     "moe_expert_ffn", "moe_combine", "moe_forward", "moe_update_bias", "moe_quantize_weights",
     "moe_quantize_act", "moe_last_error", "moe_set_timing_events", "MOE_NUM_MARKS", "MARK_NAMES", "LIB_PATH",
     "moe_balance_stats", "moe_backward_workspace_size", "moe_expert_ffn_backward_input", "moe_transpose_fp8_weights",
+    "moe_expert_ffn_backward",
 ]
 
 # MOE_LIBRARY_PATH overrides the in-tree library (a developer switch for comparing builds).
@@ -64,6 +65,7 @@ _SIGS = {
     "moe_balance_stats": [_CP, _vp, _vp, _i32, _f32, _f32, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_backward_workspace_size": [_CP, ctypes.POINTER(_sz)],
     "moe_expert_ffn_backward_input": [_CP, _LP, _LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_expert_ffn_backward": [_CP, _LP, _LP] + [_vp] * 12 + [_sz, _vp],
     "moe_transpose_fp8_weights": [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp],
     "moe_quantize_weights": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
     "moe_quantize_act": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
@@ -173,6 +175,14 @@ def moe_expert_ffn_backward_input(cfg, layer, layer_t, u, offsets, perm_src, dy_
                                   dx_shared, ws, stream=None):
     _call("moe_expert_ffn_backward_input", ctypes.byref(cfg), ctypes.byref(layer), ctypes.byref(layer_t), _dev(u),
           _dev(offsets), _dev(perm_src), _dev(dy_routed), _dev(dy_shared), _dev(dx_routed), _dev(dx_shared), _dev(ws),
+          ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+
+
+def moe_expert_ffn_backward(cfg, layer, layer_t, u, offsets, perm_src, dy_routed, dy_shared, dx_routed, dx_shared,
+                            dw13, dw2, dws13, dws2, ws, stream=None):
+    _call("moe_expert_ffn_backward", ctypes.byref(cfg), ctypes.byref(layer), ctypes.byref(layer_t), _dev(u),
+          _dev(offsets), _dev(perm_src), _dev(dy_routed), _dev(dy_shared), _dev(dx_routed), _dev(dx_shared),
+          _dev(dw13), _dev(dw2), _dev(dws13), _dev(dws2), _dev(ws),
           ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
 
 

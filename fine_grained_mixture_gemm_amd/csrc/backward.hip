@@ -5,12 +5,26 @@
 // expert, dx = [dg | dv] [W1; W3] with dg, dv the gradients of a = SiLU(g) * v; the GEMMs are the grouped
 // kernels of gemm_mfma.hip (g and v recomputed in fp32; da = dy W2 and dx with the transposed weights).
 // A transposed E4M3 weight keeps its codes and takes the transposed grid of its 128x128 block scales.
+//
+// Weight gradients (same section: the weight backward GEMM in FP8, weight gradients kept in BF16):
+// dW2 = dy^T a and d[W1; W3] = [dg | dv]^T x per expert, a contraction over the expert's rows (tokens).
+// Both operands are quantized in 1x128 tiles along the rows, starting at the expert's first row (its last
+// tile padded with zero rows), and stored transposed so the contraction is contiguous: codes
+// [channels][padded rows], scales [row block][channels]. The cached activations x and a enter as the
+// values of their forward E4M3 copies (x quantized 1x128 along d, a along f), requantized along the rows.
 #include "common.h"
 #include "kernels.h"
 
 #include <algorithm>
 
 namespace moe {
+
+// d/dg and d/dv of a = SiLU(g) * v for the upstream da, fp32.
+__device__ __forceinline__ void swiglu_grad(float da, float g, float v, float& dg, float& dv) {
+  const float sig = 1.0f / (1.0f + __expf(-g));
+  dg = da * v * sig * (1.0f + g * (1.0f - sig));
+  dv = da * g * sig;
+}
 
 // [dg | dv] of a = SiLU(g) * v for the upstream da, evaluated in fp32 and quantized 1x128 (E4M3) along
 // the 2 fg columns (dg in columns 0..fg-1, dv in fg..2fg-1). 16 lanes take one (row, 128-column block b):
@@ -39,9 +53,7 @@ __global__ __launch_bounds__(256) void swiglu_backward_quant(const float* __rest
   float dg[8], dv[8], mg = 0.f, mv = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float sig = 1.0f / (1.0f + __expf(-g8[i]));
-    dg[i] = d8[i] * v8[i] * sig * (1.0f + g8[i] * (1.0f - sig));
-    dv[i] = d8[i] * g8[i] * sig;
+    swiglu_grad(d8[i], g8[i], v8[i], dg[i], dv[i]);
     mg = fmaxf(mg, fabsf(dg[i]));
     mv = fmaxf(mv, fabsf(dv[i]));
   }
@@ -97,6 +109,304 @@ __global__ __launch_bounds__(256) void transpose_f32(const float* __restrict__ s
     const int rem = (int)(i - m * rb * cb), r = rem / cb, c = rem % cb;
     st[m * rb * cb + (long long)c * rb + r] = s[i];
   }
+}
+
+// ----------------------------------------------------------------------------- weight gradients
+constexpr int kRowBlk = 128;                       // rows per quantization tile = rows per GEMM K stage
+constexpr int kQStride = 132;                      // LDS row stride (floats) of the 128 x 128 staging tile
+constexpr int kQLds = (kRowBlk * kQStride + 2 * kRowBlk) * 4;
+
+// pblk[g] = first row block of group g (routed experts 0..E-1, then the shared block, empty unless
+// `shared`), pblk[E + 1] = their total: ceil(n_g / 128) blocks per group. One block, a scan over LDS.
+__global__ __launch_bounds__(512) void wgrad_block_prefix(const int32_t* __restrict__ offsets, int E, int T,
+                                                          int shared, int32_t* __restrict__ pblk) {
+  __shared__ int buf[512];
+  const int g = threadIdx.x;
+  int n = 0;
+  if (g < E) n = cdiv(offsets[g + 1] - offsets[g], kRowBlk);
+  else if (g == E && shared) n = cdiv(T, kRowBlk);
+  buf[g] = n;
+  __syncthreads();
+  for (int o = 1; o < 512; o <<= 1) {
+    const int v = g >= o ? buf[g - o] : 0;
+    __syncthreads();
+    buf[g] += v;
+    __syncthreads();
+  }
+  if (g <= E) pblk[g + 1] = buf[g];
+  if (g == 0) pblk[0] = 0;
+}
+
+// The group holding row block b: the last g with pblk[g] <= b (a non-empty group; b < pblk[E + 1]).
+__device__ __forceinline__ int wgrad_group_of(const int32_t* __restrict__ pblk, int E, int b) {
+  int lo = 0, hi = E + 1;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pblk[mid] <= b) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// One block per (row block b, 128-channel block): the block's rows are staged in LDS as fp32 (source
+// dependent, below), then every channel is quantized over the 128 rows and written transposed.
+//   DY : dy rows (bf16) as given;
+//   X  : u rows (bf16, routed rows gathered through perm) -> 1x128 E4M3 along the channels, as the
+//        forward quantizes them, dequantized;
+//   A  : a = SiLU(g) * v from the fp32 [g | v] rows -> the forward's 1x128 requantization, dequantized;
+//   DGV: [dg | dv] from da and [g | v] (channels < fg: dg, else dv), fp32.
+template <int SRC>
+__global__ __launch_bounds__(256) void wgrad_quant_rows(WgQuantArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float qlds[];
+  float* tile = qlds;
+  float* red = qlds + kRowBlk * kQStride;          // [2][128] half-column maxima
+  const int b = blockIdx.x, cb = blockIdx.y, tid = threadIdx.x;
+  if (b >= a.pblk[a.E + 1]) return;
+  const int grp = wgrad_group_of(a.pblk, a.E, b);
+  const bool shared = grp == a.E;
+  const int r0 = (b - a.pblk[grp]) * kRowBlk;
+  const int n = shared ? a.T : a.offsets[grp + 1] - a.offsets[grp];
+  const int nrows = min(kRowBlk, n - r0);
+  const int rowbase = (shared ? 0 : a.offsets[grp]) + r0;
+  const int c8 = (tid & 15) * 8;
+  for (int pass = 0; pass < kRowBlk / 16; ++pass) {
+    const int rr = pass * 16 + (tid >> 4);
+    float v[8];
+    if (rr < nrows) {                              // uniform over the 16 lanes of a row
+      const int row = rowbase + rr;
+      if constexpr (SRC == kWgSrcDy || SRC == kWgSrcX) {
+        const uint16_t* base = shared ? a.bf_s : a.bf_r;
+        const size_t srow = SRC == kWgSrcX && !shared ? (size_t)a.perm[row] : (size_t)row;
+        const uint4 raw = *reinterpret_cast<const uint4*>(base + srow * a.C + cb * 128 + c8);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(w[i] << 16);
+          v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+      } else if constexpr (SRC == kWgSrcA) {
+        const float* gr = (shared ? a.gv_s : a.gv_r) + (size_t)row * 2 * a.fg + cb * 128 + c8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float4 g4 = *reinterpret_cast<const float4*>(gr + 4 * h);
+          const float4 v4 = *reinterpret_cast<const float4*>(gr + a.fg + 4 * h);
+          v[4 * h] = silu(g4.x) * v4.x;
+          v[4 * h + 1] = silu(g4.y) * v4.y;
+          v[4 * h + 2] = silu(g4.z) * v4.z;
+          v[4 * h + 3] = silu(g4.w) * v4.w;
+        }
+      } else {
+        const bool up = cb * 128 >= a.fg;
+        const int c = cb * 128 - (up ? a.fg : 0) + c8;
+        const float* gr = (shared ? a.gv_s : a.gv_r) + (size_t)row * 2 * a.fg + c;
+        const float* dr = (shared ? a.da_s : a.da_r) + (size_t)row * a.fg + c;
+        float d8[8], g8[8], u8[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float4 x = *reinterpret_cast<const float4*>(dr + 4 * h);
+          const float4 y = *reinterpret_cast<const float4*>(gr + 4 * h);
+          const float4 z = *reinterpret_cast<const float4*>(gr + a.fg + 4 * h);
+          d8[4 * h] = x.x; d8[4 * h + 1] = x.y; d8[4 * h + 2] = x.z; d8[4 * h + 3] = x.w;
+          g8[4 * h] = y.x; g8[4 * h + 1] = y.y; g8[4 * h + 2] = y.z; g8[4 * h + 3] = y.w;
+          u8[4 * h] = z.x; u8[4 * h + 1] = z.y; u8[4 * h + 2] = z.z; u8[4 * h + 3] = z.w;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float dg, dv;
+          swiglu_grad(d8[k], g8[k], u8[k], dg, dv);
+          v[k] = up ? dv : dg;
+        }
+      }
+      if constexpr (SRC == kWgSrcX || SRC == kWgSrcA) {
+        float amax = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[k]));
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        float sc, inv;
+        e4m3_scales(amax, sc, inv);
+        const int q0 = (int)f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        const int q1 = (int)f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+        v[0] = __builtin_amdgcn_cvt_f32_fp8(q0, 0) * sc;
+        v[1] = __builtin_amdgcn_cvt_f32_fp8(q0, 1) * sc;
+        v[2] = __builtin_amdgcn_cvt_f32_fp8(q0, 2) * sc;
+        v[3] = __builtin_amdgcn_cvt_f32_fp8(q0, 3) * sc;
+        v[4] = __builtin_amdgcn_cvt_f32_fp8(q1, 0) * sc;
+        v[5] = __builtin_amdgcn_cvt_f32_fp8(q1, 1) * sc;
+        v[6] = __builtin_amdgcn_cvt_f32_fp8(q1, 2) * sc;
+        v[7] = __builtin_amdgcn_cvt_f32_fp8(q1, 3) * sc;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = 0.f;
+    }
+    float* t = tile + rr * kQStride + c8;
+    *reinterpret_cast<float4*>(t) = float4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<float4*>(t + 4) = float4{v[4], v[5], v[6], v[7]};
+  }
+  __syncthreads();
+  // channel c, rows 64 h .. 64 h + 63
+  const int c = tid & 127, h = tid >> 7;
+  const float* col = tile + 64 * h * kQStride + c;
+  float amax = 0.f;
+  for (int r = 0; r < 64; ++r) amax = fmaxf(amax, fabsf(col[r * kQStride]));
+  red[h * kRowBlk + c] = amax;
+  __syncthreads();
+  amax = fmaxf(red[c], red[kRowBlk + c]);
+  float sc, inv;
+  e4m3_scales(amax, sc, inv);
+  uint8_t* q = a.qt + (size_t)(cb * 128 + c) * a.rpad + (size_t)b * kRowBlk + 64 * h;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float* e = col + (16 * w + 4 * k) * kQStride;
+      o[k] = f32x4_to_e4m3x4(e[0] * inv, e[kQStride] * inv, e[2 * kQStride] * inv, e[3 * kQStride] * inv);
+    }
+    *reinterpret_cast<uint4*>(q + 16 * w) = uint4{o[0], o[1], o[2], o[3]};
+  }
+  if (h == 0) a.st[(size_t)b * a.C + cb * 128 + c] = sc;
+}
+
+// out[m][n] = sum over the group's row blocks kb of  sum_{k in kb} B[m][k] A[n][k] * sB[kb][m] sA[kb][n],
+// bf16, one 128 x 128 output tile per block (4 waves of 64 x 64). A is the MFMA A operand (output
+// columns, so a lane's four accumulators are four adjacent columns of one output row); each
+// 16x16x128 product is promoted with the product of its row's and its column's scales. Tiles of the
+// shared block (the longest contraction) come first, then the routed experts in order; inside a group
+// the larger output dimension runs fastest, so the blocks of an XCD (block id mod 8) share the smaller
+// operand and split the larger one.
+__global__ __launch_bounds__(256, 2) void grouped_wgrad_mfma(WgGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t sA[kRowBlk * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[kRowBlk * 128];
+  __shared__ __attribute__((aligned(16))) float sAs[kRowBlk];
+  __shared__ __attribute__((aligned(16))) float sBs[kRowBlk];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 1, wm = wave >> 1, tr = lane & 15, g = lane >> 4;
+  const int mtn = a.M / 128, ntn = a.N / 128, tpg = mtn * ntn;
+  const int t = blockIdx.x;
+  const int gi = t / tpg, rem = t - gi * tpg;
+  const int group = a.shared ? (gi == 0 ? a.E : gi - 1) : gi;
+  int mt, nt;
+  if (a.M > a.N) {
+    nt = rem / mtn;
+    mt = rem - nt * mtn;
+  } else {
+    mt = rem / ntn;
+    nt = rem - mt * ntn;
+  }
+  const int m0 = mt * 128, n0 = nt * 128;
+  const int kb0 = a.pblk[group], nk = a.pblk[group + 1] - kb0;
+
+  // loader: thread -> rows (tid >> 3) + 32 q, 16-byte chunk tid & 7 of both operands; scales: A (tid < 128)
+  // or B (tid >= 128)
+  const int lrow = tid >> 3, lch = tid & 7;
+  i32x4 ra[4], rb[4];
+  float rs = 0.f;
+  auto load = [&](int s) {
+    const size_t kofs = (size_t)(kb0 + s) * kRowBlk + lch * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[q] = *reinterpret_cast<const i32x4*>(a.A + (size_t)(n0 + lrow + 32 * q) * a.rpad + kofs);
+      rb[q] = *reinterpret_cast<const i32x4*>(a.B + (size_t)(m0 + lrow + 32 * q) * a.rpad + kofs);
+    }
+    rs = tid < 128 ? a.As[(size_t)(kb0 + s) * a.N + n0 + tid] : a.Bs[(size_t)(kb0 + s) * a.M + m0 + tid - 128];
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (nk > 0) load(0);
+  auto rd = [&](const uint8_t* base, int row) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + row * 128 + ((g ^ (row & 7)) * 16));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + row * 128 + (((4 + g) ^ (row & 7)) * 16));
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  for (int s = 0; s < nk; ++s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = lrow + 32 * q;
+      *reinterpret_cast<i32x4*>(sA + row * 128 + ((lch ^ (row & 7)) * 16)) = ra[q];
+      *reinterpret_cast<i32x4*>(sB + row * 128 + ((lch ^ (row & 7)) * 16)) = rb[q];
+    }
+    if (tid < 128) sAs[tid] = rs;
+    else sBs[tid - 128] = rs;
+    __syncthreads();
+    if (s + 1 < nk) load(s + 1);
+    i32x8 aa[4], bb[4];
+    f32x4 sa[4];
+    float sb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      aa[i] = rd(sA, 64 * wn + 16 * i + tr);
+      sa[i] = *reinterpret_cast<const f32x4*>(sAs + 64 * wn + 16 * i + 4 * g);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bb[j] = rd(sB, 64 * wm + 16 * j + tr);
+      sb[j] = sBs[64 * wm + 16 * j + tr];
+    }
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa[i], bb[j], zero, 0, 0, 0, 127, 0, 127);
+        acc[i][j] += (sa[i] * sb[j]) * p;
+      }
+    __syncthreads();
+  }
+  uint16_t* out = (group == a.E ? a.out_s : a.out_r + (size_t)group * a.M * a.N);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + 64 * wm + 16 * j + tr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 64 * wn + 16 * i + 4 * g;
+      uint2 v;
+      v.x = uint32_t(f32_to_bf16(acc[i][j][0])) | (uint32_t(f32_to_bf16(acc[i][j][1])) << 16);
+      v.y = uint32_t(f32_to_bf16(acc[i][j][2])) | (uint32_t(f32_to_bf16(acc[i][j][3])) << 16);
+      *reinterpret_cast<uint2*>(out + (size_t)m * a.N + n) = v;
+    }
+  }
+}
+
+int wgrad_row_blocks_max(int T, int K, int E, bool shared) {
+  return cdiv(T * K, kRowBlk) + E + (shared ? cdiv(T, kRowBlk) : 0);
+}
+
+hipError_t launch_wgrad_prefix(const int32_t* offsets, int E, int T, bool shared, int32_t* pblk, hipStream_t s) {
+  wgrad_block_prefix<<<1, 512, 0, s>>>(offsets, E, T, shared ? 1 : 0, pblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_quant(const WgQuantArgs& a, int src, int nblk_max, hipStream_t s) {
+  static bool attr_done[4] = {false, false, false, false};
+  const void* fns[4] = {(const void*)wgrad_quant_rows<kWgSrcDy>, (const void*)wgrad_quant_rows<kWgSrcX>,
+                        (const void*)wgrad_quant_rows<kWgSrcA>, (const void*)wgrad_quant_rows<kWgSrcDgv>};
+  if (src < 0 || src > 3) return hipErrorInvalidValue;
+  if (nblk_max == 0) return hipSuccess;
+  if (!attr_done[src]) {
+    const hipError_t e = hipFuncSetAttribute(fns[src], hipFuncAttributeMaxDynamicSharedMemorySize, kQLds);
+    if (e != hipSuccess) return e;
+    attr_done[src] = true;
+  }
+  const dim3 grid(nblk_max, a.C / 128);
+  switch (src) {
+    case kWgSrcDy: wgrad_quant_rows<kWgSrcDy><<<grid, 256, kQLds, s>>>(a); break;
+    case kWgSrcX: wgrad_quant_rows<kWgSrcX><<<grid, 256, kQLds, s>>>(a); break;
+    case kWgSrcA: wgrad_quant_rows<kWgSrcA><<<grid, 256, kQLds, s>>>(a); break;
+    default: wgrad_quant_rows<kWgSrcDgv><<<grid, 256, kQLds, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_gemm(const WgGemmArgs& a, hipStream_t s) {
+  const long long tiles = (long long)(a.E + (a.shared ? 1 : 0)) * (a.M / 128) * (a.N / 128);
+  if (tiles == 0) return hipSuccess;
+  grouped_wgrad_mfma<<<(unsigned)tiles, 256, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_swiglu_backward_quant(const float* da, const float* gv, int rows, int fg, uint8_t* q, float* scales,

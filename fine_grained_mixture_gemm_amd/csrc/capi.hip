@@ -183,6 +183,11 @@ int device_cus() {
 struct BwdLayout {
   size_t uq, us, mt_prefix, xsched_a, xsched_b;
   size_t dyq_r, dys_r, dyq_s, dys_s, da_r, da_s, gv_r, gv_s, dgq_r, dgs_r, dgq_s, dgs_s;
+  // weight gradients: row-block prefix, operands quantized along the rows (codes [C][rpad], scales
+  // [row block][C])
+  size_t pblk, wq_dy, ws_dy, wq_a, ws_a, wq_dgv, ws_dgv, wq_x, ws_x;
+  int nblk;
+  size_t rpad;
   size_t total;
 };
 
@@ -213,6 +218,18 @@ BwdLayout bwd_layout(const moe_config* c) {
   L.dgs_r = take(rows * (2 * f / 128) * 4);
   L.dgq_s = take(T * 2 * fs);
   L.dgs_s = take(T * (2 * fs / 128) * 4);
+  L.nblk = wgrad_row_blocks_max(c->T, c->top_k, c->n_routed, fs > 0);
+  L.rpad = (size_t)L.nblk * 128;
+  const size_t nb = L.nblk;
+  L.pblk = take((E + 2) * 4);
+  L.wq_dy = take(d * L.rpad);
+  L.ws_dy = take(nb * d * 4);
+  L.wq_a = take(f * L.rpad);
+  L.ws_a = take(nb * f * 4);
+  L.wq_dgv = take(2 * f * L.rpad);
+  L.ws_dgv = take(nb * 2 * f * 4);
+  L.wq_x = take(d * L.rpad);
+  L.ws_x = take(nb * d * 4);
   L.total = off + 256;
   return L;
 }
@@ -223,6 +240,68 @@ moe_status check_bwd_cfg(const moe_config* c) {
   if (c->n_shared > 1) return fail(MOE_ERR_UNSUPPORTED, "the expert input backward takes at most one shared expert");
   if (c->inter_dim % 256) return fail(MOE_ERR_UNSUPPORTED, "the expert input backward needs inter_dim %% 256 == 0");
   if (2 * c->inter_dim > 8192) return fail(MOE_ERR_UNSUPPORTED, "the expert input backward needs 2 * inter_dim <= 8192");
+  return MOE_OK;
+}
+
+// Weight gradients (after the g/v and da GEMMs of the backward have filled gv and da): the row-block
+// prefix, the four operands quantized along the rows, then dW2 = dy^T a and d[W1; W3] = [dg | dv]^T x.
+moe_status weight_gradients(const moe_config* c, const BwdLayout& L, uint8_t* base, const void* u,
+                            const int32_t* offsets, const int32_t* perm, const void* dy_r, const void* dy_s,
+                            void* dw13, void* dw2, void* dws13, void* dws2, hipStream_t s) {
+  const bool sh = c->n_shared > 0;
+  const int E = c->n_routed, d = c->d_model, f = c->inter_dim;
+  int32_t* pblk = reinterpret_cast<int32_t*>(base + L.pblk);
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(base + o); };
+  MOE_TRY(hip_status(launch_wgrad_prefix(offsets, E, c->T, sh, pblk, s), "row-block prefix launch"));
+  WgQuantArgs q{};
+  q.offsets = offsets;
+  q.perm = perm;
+  q.pblk = pblk;
+  q.E = E;
+  q.T = c->T;
+  q.fg = f;
+  q.rpad = L.rpad;
+  q.gv_r = F(L.gv_r);
+  q.gv_s = F(L.gv_s);
+  q.da_r = F(L.da_r);
+  q.da_s = F(L.da_s);
+  auto quant = [&](int src, int C, const void* br, const void* bs, size_t wq, size_t wsc) {
+    q.C = C;
+    q.bf_r = static_cast<const uint16_t*>(br);
+    q.bf_s = static_cast<const uint16_t*>(bs);
+    q.qt = base + wq;
+    q.st = F(wsc);
+    return hip_status(launch_wgrad_quant(q, src, L.nblk, s), "row quantization launch");
+  };
+  MOE_TRY(quant(kWgSrcDy, d, dy_r, dy_s, L.wq_dy, L.ws_dy));
+  MOE_TRY(quant(kWgSrcA, f, nullptr, nullptr, L.wq_a, L.ws_a));
+  MOE_TRY(quant(kWgSrcDgv, 2 * f, nullptr, nullptr, L.wq_dgv, L.ws_dgv));
+  MOE_TRY(quant(kWgSrcX, d, u, u, L.wq_x, L.ws_x));
+  WgGemmArgs g{};
+  g.pblk = pblk;
+  g.E = E;
+  g.shared = sh ? 1 : 0;
+  g.rpad = L.rpad;
+  // dW2 [d][f]: rows from dy, columns from a
+  g.M = d;
+  g.N = f;
+  g.A = base + L.wq_a;
+  g.As = F(L.ws_a);
+  g.B = base + L.wq_dy;
+  g.Bs = F(L.ws_dy);
+  g.out_r = static_cast<uint16_t*>(dw2);
+  g.out_s = static_cast<uint16_t*>(dws2);
+  MOE_TRY(hip_status(launch_wgrad_gemm(g, s), "dW2 GEMM launch"));
+  // d[W1; W3] [2f][d]: rows from [dg | dv], columns from x
+  g.M = 2 * f;
+  g.N = d;
+  g.A = base + L.wq_x;
+  g.As = F(L.ws_x);
+  g.B = base + L.wq_dgv;
+  g.Bs = F(L.ws_dgv);
+  g.out_r = static_cast<uint16_t*>(dw13);
+  g.out_s = static_cast<uint16_t*>(dws13);
+  MOE_TRY(hip_status(launch_wgrad_gemm(g, s), "dW13 GEMM launch"));
   return MOE_OK;
 }
 
@@ -574,22 +653,40 @@ moe_status moe_transpose_fp8_weights(const uint8_t* q, const float* scales, int3
   return hip_status(launch_transpose_fp8(q, scales, batch, rows, cols, qt, scales_t, stream), "weight transpose launch");
 }
 
-moe_status moe_expert_ffn_backward_input(const moe_config* cfg, const moe_layer* layer, const moe_layer* layer_t,
-                                         const void* u, const int32_t* offsets, const int32_t* perm_src,
-                                         const void* dy_routed, const void* dy_shared, void* dx_routed, void* dx_shared,
-                                         void* ws, size_t ws_bytes, hipStream_t stream) {
+moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer, const moe_layer* layer_t,
+                                   const void* u, const int32_t* offsets, const int32_t* perm_src, const void* dy_routed,
+                                   const void* dy_shared, void* dx_routed, void* dx_shared, void* dw13, void* dw2,
+                                   void* dws13, void* dws2, void* ws, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_bwd_cfg(cfg));
   MOE_TRY(check_layer_experts(cfg, layer));
   MOE_TRY(check_layer_experts(cfg, layer_t));
   const moe_config* c = cfg;
   const bool sh = c->n_shared > 0;
-  if (c->T > 0 && (!u || !offsets || !perm_src || !dy_routed || !dx_routed))
-    return fail(MOE_ERR_INVALID_ARG, "u / offsets / perm_src / dy_routed / dx_routed is NULL");
-  if (c->T > 0 && sh && (!dy_shared || !dx_shared)) return fail(MOE_ERR_INVALID_ARG, "dy_shared / dx_shared is NULL with n_shared > 0");
+  const bool want_dx = dx_routed != nullptr, want_dw = dw13 != nullptr;
+  if (!want_dx && !want_dw) return fail(MOE_ERR_INVALID_ARG, "neither dx_routed nor dw13 is given");
+  if (want_dw && !dw2) return fail(MOE_ERR_INVALID_ARG, "dw2 is NULL while dw13 is given");
+  if (want_dw && sh && (!dws13 || !dws2)) return fail(MOE_ERR_INVALID_ARG, "dws13 / dws2 is NULL with n_shared > 0");
+  if (c->T > 0 && (!u || !offsets || !perm_src || !dy_routed))
+    return fail(MOE_ERR_INVALID_ARG, "u / offsets / perm_src / dy_routed is NULL");
+  if (c->T > 0 && sh && !dy_shared) return fail(MOE_ERR_INVALID_ARG, "dy_shared is NULL with n_shared > 0");
+  if (want_dx && c->T > 0 && sh && !dx_shared) return fail(MOE_ERR_INVALID_ARG, "dx_shared is NULL with n_shared > 0");
   const BwdLayout L = bwd_layout(c);
   if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
-  if (c->T == 0) return MOE_OK;
+  if (c->T == 0) {
+    // no rows: every weight gradient is zero
+    if (want_dw) {
+      const size_t n13 = (size_t)c->n_routed * 2 * c->inter_dim * c->d_model * 2, n2 = n13 / 2;
+      MOE_TRY(hip_status(hipMemsetAsync(dw13, 0, n13, stream), "weight gradient clear"));
+      MOE_TRY(hip_status(hipMemsetAsync(dw2, 0, n2, stream), "weight gradient clear"));
+      if (sh) {
+        const size_t s13 = (size_t)2 * c->inter_dim * c->d_model * 2;
+        MOE_TRY(hip_status(hipMemsetAsync(dws13, 0, s13, stream), "weight gradient clear"));
+        MOE_TRY(hip_status(hipMemsetAsync(dws2, 0, s13 / 2, stream), "weight gradient clear"));
+      }
+    }
+    return MOE_OK;
+  }
   uint8_t* base = reinterpret_cast<uint8_t*>(align_up(reinterpret_cast<uintptr_t>(ws), 256));
   hipStream_t s = stream;
   const int T = c->T, E = c->n_routed, d = c->d_model, f = c->inter_dim, fs = c->n_shared * f;
@@ -648,6 +745,8 @@ moe_status moe_expert_ffn_backward_input(const moe_config* cfg, const moe_layer*
   g.out_routed = base + L.da_r;
   g.out_shared = base + L.da_s;
   MOE_TRY(hip_status(launch_gemm_mfma(g, true, false, grid, s, true), "da GEMM launch"));
+  if (want_dw) MOE_TRY(weight_gradients(c, L, base, u, offsets, perm_src, dy_routed, dy_shared, dw13, dw2, dws13, dws2, s));
+  if (!want_dx) return MOE_OK;
   // 3. [dg | dv] from da, g, v, quantized 1x128 along 2f
   MOE_TRY(hip_status(launch_swiglu_backward_quant(F(L.da_r), F(L.gv_r), rows, f, base + L.dgq_r, F(L.dgs_r), s),
                      "SwiGLU backward launch"));
@@ -672,6 +771,16 @@ moe_status moe_expert_ffn_backward_input(const moe_config* cfg, const moe_layer*
   g.out_shared = static_cast<uint8_t*>(dx_shared);
   MOE_TRY(hip_status(launch_gemm_mfma(g, true, false, grid, s, false), "dx GEMM launch"));
   return MOE_OK;
+}
+
+moe_status moe_expert_ffn_backward_input(const moe_config* cfg, const moe_layer* layer, const moe_layer* layer_t,
+                                         const void* u, const int32_t* offsets, const int32_t* perm_src,
+                                         const void* dy_routed, const void* dy_shared, void* dx_routed, void* dx_shared,
+                                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dx_routed && cfg && cfg->T > 0) return fail(MOE_ERR_INVALID_ARG, "dx_routed is NULL");
+  if (!dx_routed) return check_bwd_cfg(cfg);
+  return moe_expert_ffn_backward(cfg, layer, layer_t, u, offsets, perm_src, dy_routed, dy_shared, dx_routed, dx_shared,
+                                 nullptr, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 moe_status moe_quantize_weights(const float* w, int32_t batch, int32_t rows, int32_t cols, uint8_t* q, float* scales,

@@ -112,6 +112,39 @@ hipError_t launch_swiglu_backward_quant(const float* da, const float* gv, int ro
                                         hipStream_t s);
 hipError_t launch_transpose_fp8(const uint8_t* q, const float* scales, int batch, int rows, int cols, uint8_t* qt,
                                 float* scales_t, hipStream_t s);
+// Weight gradients of the E4M3 experts: row-block prefix, quantization along the rows (transposed
+// out), and the grouped row-scaled GEMM.
+enum { kWgSrcDy = 0, kWgSrcX = 1, kWgSrcA = 2, kWgSrcDgv = 3 };
+struct WgQuantArgs {
+  const int32_t* offsets;     // [E+1] routed row offsets
+  const int32_t* perm;        // [T*K] token of each routed row (source X)
+  const int32_t* pblk;        // [E+2] row-block prefix (routed experts, then the shared block)
+  int E, T, C, fg;            // C channels of the operand; fg inner dim of [g | v] and da
+  const uint16_t* bf_r;       // DY: dy_routed [T*K][C]; X: u [T][C]
+  const uint16_t* bf_s;       // DY: dy_shared [T][C]; X: u
+  const float* gv_r;          // A, DGV: [g | v] rows [.][2 fg]
+  const float* gv_s;
+  const float* da_r;          // DGV: da rows [.][fg]
+  const float* da_s;
+  uint8_t* qt;                // codes [C][rpad]
+  float* st;                  // scales [row block][C]
+  size_t rpad;                // padded rows of qt (row stride)
+};
+struct WgGemmArgs {
+  const int32_t* pblk;
+  int E, shared, M, N;        // output [M][N] per group (multiples of 128)
+  const uint8_t* A;           // [N][rpad] codes, scales As [row block][N]
+  const float* As;
+  const uint8_t* B;           // [M][rpad] codes, scales Bs [row block][M]
+  const float* Bs;
+  size_t rpad;
+  uint16_t* out_r;            // bf16 [E][M][N]
+  uint16_t* out_s;            // bf16 [M][N]
+};
+int wgrad_row_blocks_max(int T, int K, int E, bool shared);
+hipError_t launch_wgrad_prefix(const int32_t* offsets, int E, int T, bool shared, int32_t* pblk, hipStream_t s);
+hipError_t launch_wgrad_quant(const WgQuantArgs& a, int src, int nblk_max, hipStream_t s);
+hipError_t launch_wgrad_gemm(const WgGemmArgs& a, hipStream_t s);
 int balance_chunks_for(int T);
 int balance_sequences_max(int T);   // sequences of T tokens when seq_len is T or a multiple of 64
 hipError_t launch_balance_stats(const BalanceArgs& a, hipStream_t s);

@@ -178,12 +178,35 @@ moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float g
  *  u [T, d] bf16 (the layer input), offsets / perm_src as moe_dispatch returns them.
  *  dy_routed [T*K, d] bf16, dy_shared [T, d] bf16 (n_shared == 1); dx_routed [T*K, d] bf16 out,
  *  dx_shared [T, d] bf16 out.
- *  ws / ws_bytes: a workspace of at least moe_backward_workspace_size bytes. */
+ *  ws / ws_bytes: a workspace of at least moe_backward_workspace_size bytes (it covers the weight
+ *  gradients of moe_expert_ffn_backward as well). */
 moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes);
 moe_status moe_expert_ffn_backward_input(const moe_config* cfg, const moe_layer* layer, const moe_layer* layer_t,
                                          const void* u, const int32_t* offsets, const int32_t* perm_src,
                                          const void* dy_routed, const void* dy_shared, void* dx_routed,
                                          void* dx_shared, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The full backward of the E4M3 experts: the input gradients above and/or the weight gradients
+ * (DeepSeek Technical Report: MoE Architecture, 3.6: the weight backward GEMM in FP8 as well, weight
+ * gradients kept in BF16). For every routed expert e over its rows (dispatch order) and for the shared
+ * block over all T tokens:
+ *   dW2      = dy^T a                [d, f]     a = SiLU(g) * v
+ *   d[W1;W3] = [dg | dv]^T x         [2f, d]    (W1 rows first, the layout of w13)
+ * with g, v, da, dg, dv as in moe_expert_ffn_backward_input. The contraction runs over the rows, so both
+ * operands are quantized in 1x128 tiles along the rows, starting at the expert's first row (the last
+ * tile padded with zero rows), promoted every 128 rows with the product of the two tiles' scales. The
+ * cached activations enter as the values of their forward E4M3 copies: x quantized 1x128 along d, a
+ * requantized 1x128 along f (as moe_expert_ffn does), each dequantized and requantized along the rows;
+ * dy as given, [dg | dv] in fp32. An expert with no rows gets a zero gradient.
+ *  dx_routed / dx_shared  as moe_expert_ffn_backward_input, or dx_routed = NULL to skip the input gradients.
+ *  dw13 [E, 2f, d] bf16 and dw2 [E, d, f] bf16 out (the layouts of layer->w13 / w2), dws13 [2f, d] and
+ *           dws2 [d, f] for the shared block (n_shared == 1), or dw13 = NULL to skip the weight gradients.
+ *  At least one of dx_routed and dw13 is given (else MOE_ERR_INVALID_ARG). Outputs are overwritten, not
+ *  accumulated. Other arguments, the workspace (moe_backward_workspace_size) and the limits as above. */
+moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer, const moe_layer* layer_t,
+                                   const void* u, const int32_t* offsets, const int32_t* perm_src, const void* dy_routed,
+                                   const void* dy_shared, void* dx_routed, void* dx_shared, void* dw13, void* dw2,
+                                   void* dws13, void* dws2, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Transpose a batch of E4M3 matrices with their 128x128 block scales: qt[m] = q[m]^T ([cols, rows]),
  * scales_t[m] = scales[m]^T ([cols/128, rows/128]); the codes are unchanged, so a transposed block keeps

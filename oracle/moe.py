@@ -234,7 +234,7 @@ def swiglu_ffn_backward_weight(dy, x, w1, w3, w2):
     return dg.T @ x, dv.T @ x, dy.T @ (silu(g) * v)
 
 
-def swiglu_ffn_backward_weight_fp8(dy, x, w13q, w13s, w2q, w2s):
+def swiglu_ffn_backward_weight_fp8(dy, x, w13q, w13s, w2q, w2s, operands: bool = False):
     """The weight-gradient GEMMs of the SwiGLU expert in E4M3 ([TR] §3.6: the weight backward GEMM runs
     in FP8, activations cached for the backward are FP8, weight gradients are kept in BF16).
 
@@ -244,7 +244,8 @@ def swiglu_ffn_backward_weight_fp8(dy, x, w13q, w13s, w2q, w2s):
     forward E4M3 copies hold: x as its 1x128 quantization along d, a = SiLU(g) * v as its 1x128
     requantization along f, each dequantized (rounded to fp32) and requantized along the rows. dy enters
     as given, [dg | dv] as its fp32 value from the input backward (swiglu_ffn_backward_input_fp8).
-    Returns (dW13 [2f, d] with the W1 rows first, dW2 [d, f]) in float64, before the BF16 rounding.
+    Returns (dW13 [2f, d] with the W1 rows first, dW2 [d, f]) in float64, before the BF16 rounding; with
+    ``operands`` also a dict of the quantizer inputs and outputs (for tests that bound rounding flips).
     """
     f = w13q.shape[0] // 2
     xq, xs = quant.quantize_act_1x128(x)
@@ -256,10 +257,15 @@ def swiglu_ffn_backward_weight_fp8(dy, x, w13q, w13s, w2q, w2s):
     da = quant.gemm_blockscaled(dyq, dys, np.ascontiguousarray(w2q.T), np.ascontiguousarray(w2s.T))
     dg, dv = swiglu_backward(da, g, v)
     dgv = np.hstack([dg, dv]).astype(np.float32)
-    dw2 = quant.gemm_rowscaled(*quant.quantize_act_along_rows(dy32),
-                               *quant.quantize_act_along_rows(quant.dequant_act(aq, as_)))
-    dw13 = quant.gemm_rowscaled(*quant.quantize_act_along_rows(dgv),
-                                *quant.quantize_act_along_rows(quant.dequant_act(xq, xs)))
+    a_deq = quant.dequant_act(aq, as_).astype(np.float32)
+    x_deq = quant.dequant_act(xq, xs).astype(np.float32)
+    dy_t, a_t = quant.quantize_act_along_rows(dy32), quant.quantize_act_along_rows(a_deq)
+    dgv_t, x_t = quant.quantize_act_along_rows(dgv), quant.quantize_act_along_rows(x_deq)
+    dw2 = quant.gemm_rowscaled(*dy_t, *a_t)
+    dw13 = quant.gemm_rowscaled(*dgv_t, *x_t)
+    if operands:
+        return dw13, dw2, dict(a32=(silu(g) * v).astype(np.float32), a_fwd=(aq, as_), a_deq=a_deq, a_t=a_t,
+                               dy_t=dy_t, dgv32=dgv, dgv_t=dgv_t, x_deq=x_deq, x_t=x_t)
     return dw13, dw2
 
 

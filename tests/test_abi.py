@@ -154,3 +154,23 @@ def test_backward_argument_errors():
     assert lib.moe_transpose_fp8_weights(16, 16, 1, 192, 128, 16, 16, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_transpose_fp8_weights(16, 16, -1, 128, 128, 16, 16, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_transpose_fp8_weights(None, 16, 1, 128, 128, 16, 16, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_full_backward_argument_errors():
+    cfg = _cfg(inter_dim=256)
+    need = moe.moe_backward_workspace_size(cfg)
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    P = ctypes.POINTER
+    lib.moe_expert_ffn_backward.argtypes = ([P(moe.moe_config), P(moe.moe_layer), P(moe.moe_layer)] +
+                                            [ctypes.c_void_p] * 12 + [ctypes.c_size_t, ctypes.c_void_p])
+    full = moe.moe_layer(16, 16, 16, 16, 16, 16, 16, 16, 16, None)
+    def call(dx=16, dxs=16, dw13=16, dw2=16, dws13=16, dws2=16, nbytes=need):
+        return lib.moe_expert_ffn_backward(ctypes.byref(cfg), ctypes.byref(full), ctypes.byref(full), 16, 16, 16, 16, 16,
+                                           dx, dxs, dw13, dw2, dws13, dws2, 16, nbytes, None)
+    assert call(dx=None, dw13=None) == moe.MOE_ERR_INVALID_ARG        # nothing asked for
+    assert call(dw2=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(dws2=None) == moe.MOE_ERR_INVALID_ARG                 # shared block needs its gradients
+    assert call(dx=None, dws13=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(dxs=None, dw13=None) == moe.MOE_ERR_INVALID_ARG       # shared dx missing
+    assert call(nbytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert "dw" in moe.moe_last_error() or "workspace" in moe.moe_last_error()
