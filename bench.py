@@ -35,6 +35,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the E4M3 expert backward")
     ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens of the workload the oracle runs")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size kernel that profiler "
@@ -129,6 +130,78 @@ def time_balance_stats(moe, L, w, ws, reps=20):
     torch.cuda.synchronize()
     return {"ms": round(e0.elapsed_time(e1) / reps, 4), "seq_len": seq,
             "loss_expert": float(loss[0]), "loss_seq": float(loss[1])}
+
+
+def time_backward(moe, L, w, ws, reps=5):
+    """Time the E4M3 expert backward on the workload's routing with a seeded bf16 gradient (not part of
+    the step): moe_expert_ffn_backward_input, and moe_expert_ffn_backward with the weight gradients too.
+    Algorithmic FLOPs per row (routed and shared): input 10 d f (g/v recompute 4 d f, da 2 d f, dx 4 d f),
+    weights 6 d f (dW2 2 d f, d[W1; W3] 4 d f)."""
+    import torch
+    dev = "cuda"
+    t = L.t
+
+    def tr(q, s):
+        qt = torch.empty(q.shape[:-2] + (q.shape[-1], q.shape[-2]), dtype=torch.uint8, device=dev)
+        st = torch.empty(s.shape[:-2] + (s.shape[-1], s.shape[-2]), dtype=torch.float32, device=dev)
+        moe.moe_transpose_fp8_weights(q, s, qt, st)
+        return qt, st
+
+    tt = {}
+    tt["w13"], tt["w13s"] = tr(t["w13"], t["w13s"])
+    tt["w2"], tt["w2s"] = tr(t["w2"], t["w2s"])
+    if w.Ks > 0:
+        tt["ws13"], tt["ws13s"] = tr(t["ws13"], t["ws13s"])
+        tt["ws2"], tt["ws2s"] = tr(t["ws2"], t["ws2s"])
+    layer_t = moe.make_layer(tt["w13"], tt["w2"], t["wg"], ws13=tt.get("ws13"), ws2=tt.get("ws2"),
+                             w13_scale=tt["w13s"], w2_scale=tt["w2s"], ws13_scale=tt.get("ws13s"),
+                             ws2_scale=tt.get("ws2s"))
+    idx = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
+    gw = torch.empty((w.T, w.K), dtype=torch.float32, device=dev)
+    counts = torch.empty(w.E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(w.E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(w.T * w.K, dtype=torch.int32, device=dev)
+    row_of = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
+    moe.moe_route(L.cfg, L.layer, t["u"], t["bias"], idx, gw, ws)
+    moe.moe_dispatch(L.cfg, idx, counts, offsets, perm, row_of, ws)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    dy_r = torch.randn((w.T * w.K, w.d), generator=g, device=dev).to(torch.bfloat16)
+    dy_s = torch.randn((w.T, w.d), generator=g, device=dev).to(torch.bfloat16) if w.Ks > 0 else None
+    dx_r = torch.empty((w.T * w.K, w.d), **bf)
+    dx_s = torch.empty((w.T, w.d), **bf) if w.Ks > 0 else None
+    dw13 = torch.empty((w.E, 2 * w.f, w.d), **bf)
+    dw2 = torch.empty((w.E, w.d, w.f), **bf)
+    dws13 = torch.empty((2 * w.fs, w.d), **bf) if w.Ks > 0 else None
+    dws2 = torch.empty((w.d, w.fs), **bf) if w.Ks > 0 else None
+    bws = torch.empty(moe.moe_backward_workspace_size(L.cfg), dtype=torch.uint8, device=dev)
+    run_in = lambda: moe.moe_expert_ffn_backward_input(L.cfg, L.layer, layer_t, t["u"], offsets, perm, dy_r, dy_s,
+                                                       dx_r, dx_s, bws)
+    run_all = lambda: moe.moe_expert_ffn_backward(L.cfg, L.layer, layer_t, t["u"], offsets, perm, dy_r, dy_s, dx_r,
+                                                  dx_s, dw13, dw2, dws13, dws2, bws)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_in, ms_all = timed(run_in), timed(run_all)
+    rows = w.T * w.K + (w.T if w.Ks > 0 else 0)
+    f_in, f_w = 10.0 * w.d * w.f * rows, 6.0 * w.d * w.f * rows
+    out = {"ms_input": round(ms_in, 3), "ms_input_and_weight": round(ms_all, 3),
+           "input_tflops": round(f_in / (ms_in * 1e-3) / 1e12, 1),
+           "input_and_weight_tflops": round((f_in + f_w) / (ms_all * 1e-3) / 1e12, 1),
+           "weight_grad_bytes_bf16": int(2 * 3 * w.d * w.f * (w.E + (1 if w.Ks > 0 else 0)))}
+    del tt, layer_t, dy_r, dy_s, dx_r, dx_s, dw13, dw2, dws13, dws2, bws
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_model():
@@ -276,6 +349,8 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     out["balance_stats"] = time_balance_stats(moe, L, w, ws)
+    if w.wdt == "fp8" and not args.no_backward:
+        out["backward"] = time_backward(moe, L, w, ws)
     prof = profiled_traffic(w.name)
     if prof is not None:
         out["roofline"]["traffic"] = round(prof["gateup"]["traffic_bytes"])

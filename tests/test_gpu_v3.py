@@ -129,3 +129,50 @@ def test_v3_decode_step_and_bias_update():
     got = b.cpu().numpy()
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
     assert (got != bias).any()
+
+
+STREAM_DY_R, STREAM_DY_S = 10_000, 10_001     # seeded output gradients of the backward check
+
+
+def test_v3_backward_sampled_experts():
+    """The E4M3 expert backward (input and weight gradients) at the V3 size, in the launch bench.py times,
+    checked on the largest, a median and the smallest non-empty expert (the shared block's gradients are
+    checked at the smaller sizes of test_gpu_backward.py); experts with no rows get zero weight gradients."""
+    from synth import device as sdev, gen
+    from tests.test_gpu_backward import _check_wgrad, _transposed_layer
+    w = configs.WORKLOADS["v3_fp8"]
+    print("[case] v3_fp8 backward, sampled experts", flush=True)
+    L = layers.device_layer(w)
+    g = H.GpuLayer(w, L.cfg, L.layer, L.t, None, None, None, None)
+    ws = H.workspace(g)
+    o = H.run_stages(g, ws)
+    layer_t, tt = _transposed_layer(g)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    dy_r = sdev.fill_normal(torch.empty((w.T * w.K, w.d), **bf), w.seed, STREAM_DY_R, 1.0)
+    dy_s = sdev.fill_normal(torch.empty((w.T, w.d), **bf), w.seed, STREAM_DY_S, 1.0)
+    dx_r, dx_s = torch.empty((w.T * w.K, w.d), **bf), torch.empty((w.T, w.d), **bf)
+    dw13, dw2 = torch.empty((w.E, 2 * w.f, w.d), **bf), torch.empty((w.E, w.d, w.f), **bf)
+    dws13, dws2 = torch.empty((2 * w.fs, w.d), **bf), torch.empty((w.d, w.fs), **bf)
+    bws = torch.empty(moe.moe_backward_workspace_size(L.cfg), dtype=torch.uint8, device="cuda")
+    moe.moe_expert_ffn_backward(L.cfg, L.layer, layer_t, L.t["u"], o["offsets"], o["perm"], dy_r, dy_s, dx_r, dx_s,
+                                dw13, dw2, dws13, dws2, bws)
+    torch.cuda.synchronize()
+    offsets, perm = H.to_np(o["offsets"]), H.to_np(o["perm"])
+    counts = np.diff(offsets)
+    for e in np.flatnonzero(counts == 0):
+        assert torch.count_nonzero(dw13[e]).item() == 0 and torch.count_nonzero(dw2[e]).item() == 0
+    nz = np.flatnonzero(counts)
+    sel = sorted({int(np.argmax(counts)), int(nz[np.argmin(counts[nz])]), int(np.argsort(counts)[len(counts) // 2])})
+    u = configs.u_as_f32(w, configs.make_u(w))
+    for e in sel:
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        dy = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(gen.normal_f32(w.seed, STREAM_DY_R, (b - a, w.d), 1.0,
+                                                                      start=a * w.d))).astype(np.float64)
+        assert np.array_equal(H.to_np(dy_r[a:b]), dy), "device and host gradient generators disagree"
+        ex = _oracle_expert(w.seed, e)
+        x = u[perm[a:b]]
+        e_dx = H.err(H.to_np(dx_r[a:b]), omoe.swiglu_ffn_backward_input_fp8(dy, x, *ex))
+        ref13, ref2, ops = omoe.swiglu_ffn_backward_weight_fp8(dy, x, *ex, operands=True)
+        worst = _check_wgrad(H.to_np(dw13[e]), H.to_np(dw2[e]), ref13, ref2, ops, b - a, f"expert {e}")
+        print(f"expert {e}: {b - a} rows, dx err {e_dx:.4f}, dW plain max-abs/RMS {worst:.4f}", flush=True)
+        assert e_dx <= H.TOL["fp8"]
