@@ -272,15 +272,17 @@ __global__ __launch_bounds__(256) void wgrad_quant_rows(WgQuantArgs a) {
 // out[m][n] = sum over the group's row blocks kb of  sum_{k in kb} B[m][k] A[n][k] * sB[kb][m] sA[kb][n],
 // bf16, one 128 x 128 output tile per block (4 waves of 64 x 64). A is the MFMA A operand (output
 // columns, so a lane's four accumulators are four adjacent columns of one output row); each
-// 16x16x128 product is promoted with the product of its row's and its column's scales. Tiles of the
-// shared block (the longest contraction) come first, then the routed experts in order; inside a group
-// the larger output dimension runs fastest, so the blocks of an XCD (block id mod 8) share the smaller
-// operand and split the larger one.
-__global__ __launch_bounds__(256, 2) void grouped_wgrad_mfma(WgGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[kRowBlk * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[kRowBlk * 128];
-  __shared__ __attribute__((aligned(16))) float sAs[kRowBlk];
-  __shared__ __attribute__((aligned(16))) float sBs[kRowBlk];
+// 16x16x128 product is promoted with the product of its row's and its column's scales. Operands go
+// global -> LDS by LDS-DMA into one buffer (16-byte chunks XOR-swizzled by row), three blocks per CU
+// overlap each other's waits. Tiles of the shared block (the longest contraction) come first, then the
+// routed experts in order; inside a group the larger output dimension runs fastest, so the blocks of
+// an XCD (block id mod 8) share the smaller operand and split the larger one.
+__global__ __launch_bounds__(256, 3) void grouped_wgrad_mfma(WgGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kRowBlk * 128 + 2 * kRowBlk * 4];
+  uint8_t* sA = lds;
+  uint8_t* sB = lds + kRowBlk * 128;
+  float* sAs = reinterpret_cast<float*>(lds + 2 * kRowBlk * 128);
+  float* sBs = sAs + kRowBlk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1, tr = lane & 15, g = lane >> 4;
   const int mtn = a.M / 128, ntn = a.N / 128, tpg = mtn * ntn;
@@ -297,65 +299,53 @@ __global__ __launch_bounds__(256, 2) void grouped_wgrad_mfma(WgGemmArgs a) {
   }
   const int m0 = mt * 128, n0 = nt * 128;
   const int kb0 = a.pblk[group], nk = a.pblk[group + 1] - kb0;
-
-  // loader: thread -> rows (tid >> 3) + 32 q, 16-byte chunk tid & 7 of both operands; scales: A (tid < 128)
-  // or B (tid >= 128)
-  const int lrow = tid >> 3, lch = tid & 7;
-  i32x4 ra[4], rb[4];
-  float rs = 0.f;
-  auto load = [&](int s) {
-    const size_t kofs = (size_t)(kb0 + s) * kRowBlk + lch * 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ra[q] = *reinterpret_cast<const i32x4*>(a.A + (size_t)(n0 + lrow + 32 * q) * a.rpad + kofs);
-      rb[q] = *reinterpret_cast<const i32x4*>(a.B + (size_t)(m0 + lrow + 32 * q) * a.rpad + kofs);
-    }
-    rs = tid < 128 ? a.As[(size_t)(kb0 + s) * a.N + n0 + tid] : a.Bs[(size_t)(kb0 + s) * a.M + m0 + tid - 128];
-  };
+  // copy geometry: piece 256 q + tid lands at LDS row (256 q + tid) / 8, position tid % 8, which holds
+  // global chunk (tid % 8) ^ (row & 7)
+  const int prow = tid >> 3, pchunk = ((tid & 7) ^ (prow & 7)) * 16;
+  const uint8_t* gA = a.A + (size_t)(n0 + prow) * a.rpad + pchunk;
+  const uint8_t* gB = a.B + (size_t)(m0 + prow) * a.rpad + pchunk;
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (nk > 0) load(0);
   auto rd = [&](const uint8_t* base, int row) {
     const i32x4 lo = *reinterpret_cast<const i32x4*>(base + row * 128 + ((g ^ (row & 7)) * 16));
     const i32x4 hi = *reinterpret_cast<const i32x4*>(base + row * 128 + (((4 + g) ^ (row & 7)) * 16));
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
   for (int s = 0; s < nk; ++s) {
+    const size_t kofs = (size_t)(kb0 + s) * kRowBlk;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int row = lrow + 32 * q;
-      *reinterpret_cast<i32x4*>(sA + row * 128 + ((lch ^ (row & 7)) * 16)) = ra[q];
-      *reinterpret_cast<i32x4*>(sB + row * 128 + ((lch ^ (row & 7)) * 16)) = rb[q];
+      dma16(gA + (size_t)(32 * q) * a.rpad + kofs, sA + (q * 256 + wave * 64) * 16);
+      dma16(gB + (size_t)(32 * q) * a.rpad + kofs, sB + (q * 256 + wave * 64) * 16);
     }
-    if (tid < 128) sAs[tid] = rs;
-    else sBs[tid - 128] = rs;
-    __syncthreads();
-    if (s + 1 < nk) load(s + 1);
-    i32x8 aa[4], bb[4];
+    if (wave < 2)
+      dma4(a.As + (size_t)(kb0 + s) * a.N + n0 + wave * 64 + lane, reinterpret_cast<uint8_t*>(sAs) + wave * 256);
+    else
+      dma4(a.Bs + (size_t)(kb0 + s) * a.M + m0 + (wave - 2) * 64 + lane, reinterpret_cast<uint8_t*>(sBs) + (wave - 2) * 256);
+    wait_vm0();
+    barrier_lds();
+    i32x8 aa[4];
     f32x4 sa[4];
-    float sb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       aa[i] = rd(sA, 64 * wn + 16 * i + tr);
       sa[i] = *reinterpret_cast<const f32x4*>(sAs + 64 * wn + 16 * i + 4 * g);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bb[j] = rd(sB, 64 * wm + 16 * j + tr);
-      sb[j] = sBs[64 * wm + 16 * j + tr];
-    }
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      const i32x8 bb = rd(sB, 64 * wm + 16 * j + tr);
+      const float sb = sBs[64 * wm + 16 * j + tr];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa[i], bb[j], zero, 0, 0, 0, 127, 0, 127);
-        acc[i][j] += (sa[i] * sb[j]) * p;
+        const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa[i], bb, zero, 0, 0, 0, 127, 0, 127);
+        acc[i][j] += (sa[i] * sb) * p;
       }
-    __syncthreads();
+    }
+    barrier_lds();   // every wave is done with the buffer before the next stage's copies land in it
   }
   uint16_t* out = (group == a.E ? a.out_s : a.out_r + (size_t)group * a.M * a.N);
 #pragma unroll

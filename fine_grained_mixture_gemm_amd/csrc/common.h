@@ -96,6 +96,30 @@ __device__ __forceinline__ uint64_t f64_order(double x) {
   return (b & 0x8000000000000000ull) ? ~b : (b | 0x8000000000000000ull);
 }
 
+// ------------------------------------------------------------------ LDS-DMA copies and waits
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Global -> LDS copy of 16 (or 4) bytes per lane; the wave writes 64 consecutive pieces at `lds_base`.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 4, 0, 0);
+}
+
+// Wait until this wave has no vector-memory operation in flight (its LDS-DMA copies have landed).
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
+
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations (lgkmcnt 0); the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ __forceinline__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -53,31 +53,9 @@ constexpr int kIds = kTab + 2 * kMaxGroups * 4 + 8;   // ring of the block's nex
 constexpr int kLdsBytes = kIds + 16;
 static_assert(kBW == kBM && kChunks == 4 && kLdsBytes <= 160 * 1024, "geometry");
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Global -> LDS copy of 16 (or 4) bytes per lane; the wave writes 64 consecutive pieces at `lds_base`.
-__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_base, 4, 0, 0);
-}
-
-// Wait until this wave has no vector-memory operation in flight (its LDS-DMA copies have landed).
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
-
-// Workgroup barrier for LDS traffic: waits for this wave's LDS operations (lgkmcnt 0); the empty asm
-// statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Tile id -> (group, N tile, rows), from LDS copies of mt_prefix and offsets: routed experts ascending,
-// N index fastest within an expert (the N tiles of one M tile share its token rows and run for equally
-// many stages, so blocks that take them together stay in step and read those rows from L2), then the
+// M index fastest within an expert (the M tiles of one N tile share its weight rows: blocks that take
+// them together start on the same weight stream, so later ones often find it in the XCD's L2), then the
 // shared group in the same order.
 __device__ __forceinline__ TileInfo decode_tile_lds(int id, const int32_t* mtp, const int32_t* off, int E, int T,
                                                     int nt_r, int nt_s) {
@@ -93,8 +71,9 @@ __device__ __forceinline__ TileInfo decode_tile_lds(int id, const int32_t* mtp, 
     const int e = __builtin_amdgcn_readfirstlane(lo);
     const int local = id - mtp[e] * nt_r;
     ti.group = e;
-    const int m_tile = local / nt_r;
-    ti.n_tile = local - m_tile * nt_r;
+    const int mt_e = mtp[e + 1] - mtp[e];
+    ti.n_tile = local / mt_e;
+    const int m_tile = local - ti.n_tile * mt_e;
     const int o0 = off[e], n_e = off[e + 1] - o0;
     ti.row0 = m_tile * kBM;
     ti.nrows = min(kBM, n_e - ti.row0);
@@ -102,8 +81,9 @@ __device__ __forceinline__ TileInfo decode_tile_lds(int id, const int32_t* mtp, 
   } else {
     const int local = id - routed_tiles;
     ti.group = E;
-    const int m_tile = local / nt_s;
-    ti.n_tile = local - m_tile * nt_s;
+    const int mt_s = (T + kBM - 1) / kBM;
+    ti.n_tile = local / mt_s;
+    const int m_tile = local - ti.n_tile * mt_s;
     ti.row0 = m_tile * kBM;
     ti.nrows = min(kBM, T - ti.row0);
     ti.rowbase = ti.row0;

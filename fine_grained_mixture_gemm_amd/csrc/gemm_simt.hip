@@ -31,8 +31,8 @@ hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_pr
   return hipGetLastError();
 }
 
-// Schedule of the matrix-core grouped GEMMs. The tile list (routed experts ascending, N index fastest
-// within an M tile, then the shared group) is cut into eight contiguous ranges of equal estimated
+// Schedule of the matrix-core grouped GEMMs. The tile list (routed experts ascending, M index fastest
+// within an N tile, then the shared group) is cut into eight contiguous ranges of equal estimated
 // cost, one per XCD; a tile costs 10 when more than half of its bm rows are valid (both token halves
 // of the block multiply) and 7 otherwise (one half multiplies; streaming its weights still takes most
 // of the time). Within a range the blocks of that XCD take tiles in order from a counter.
@@ -92,8 +92,8 @@ __global__ __launch_bounds__(512) void ffn_schedule_mfma(const int32_t* __restri
       r[8] = (int)s_tot[1];
     }
     // boundary x: the first tile whose preceding cost reaches x * total / 8. The groups with tiles split
-    // (0, total] into the intervals (before, before + C]; the owner scans its rows of nt equal tiles (N
-    // fastest within an M tile) and divides within the row.
+    // (0, total] into the intervals (before, before + C]; the owner's tiles are nt equal columns of cost S
+    // (M fastest within an N column): it skips whole columns, then scans the M tiles of the next one.
     for (int x = 1; x < 8; ++x) {
       const long long tgt = total * x / 8;
       if (tgt <= 0) {
@@ -102,11 +102,11 @@ __global__ __launch_bounds__(512) void ffn_schedule_mfma(const int32_t* __restri
       }
       if (C > 0 && before < tgt && tgt <= before + C) {
         const long long off = tgt - before;
+        const long long nf = off / S;        // whole N columns (each S) before the boundary
+        long long cum = nf * S;
         int mi = 0;
-        long long cum = 0;
-        while (mi < mt && cum + (long long)nt * tile_cost(n, mi) < off) cum += (long long)nt * tile_cost(n, mi++);
-        const int ni = mi < mt ? (int)((off - cum + tile_cost(n, mi) - 1) / tile_cost(n, mi)) : 0;
-        r[x] = (int)(id0 + (long long)mi * nt + ni);
+        while (cum < off) cum += tile_cost(n, mi++);
+        r[x] = (int)(id0 + nf * mt + mi);
       }
     }
     __syncthreads();   // s_tot is written again by the next launch's totals
