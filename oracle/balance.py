@@ -7,7 +7,7 @@ alpha_1 = 0.003 (V2). [TR] §3.3 and [YJ] §4.3 add, for V3, a sequence-wise bal
 small weight (alpha = 0.0001) whose formula is not printed.
 
 Readings taken here (repeated where used):
-* f_i = (tokens whose top-K contains i) / T. The pages say "fraction of tokens"; no normalisation by
+* f_i = (tokens whose top-K contains i) / T. The pages define f_i as a share of the tokens; no normalisation by
   E/K is printed, so none is applied (sum_i f_i = K).
 * P_i = (1/T) sum_t s_{i,t}, the routing probability over all routed experts: the softmax of the logits
   in softmax mode; in sigmoid mode the affinities sigmoid(z) normalised over all routed experts (the

@@ -204,8 +204,8 @@ def swiglu_ffn_backward_input(dy, x, w1, w3, w2) -> np.ndarray:
 
 
 def swiglu_ffn_backward_input_fp8(dy, x, w13q, w13s, w2q, w2s) -> np.ndarray:
-    """The activation backward GEMMs of the SwiGLU expert in E4M3 ([TR] §3.6: "activation backward
-    GEMM" in FP8, 1x128 activation tiles, 128x128 weight blocks, promotion every 128).
+    """The activation backward GEMMs of the SwiGLU expert in E4M3 ([TR] §3.6: the GEMMs of the
+    activation gradients run in FP8, 1x128 activation tiles, 128x128 weight blocks, promotion every 128).
 
     Readings (the pages fix the formats, not the dataflow): the cached forward input x is quantized
     1x128 as in the forward and g, v are recomputed from it with the forward GEMM; the output gradient
