@@ -113,8 +113,22 @@ __global__ __launch_bounds__(256) void transpose_f32(const float* __restrict__ s
 
 // ----------------------------------------------------------------------------- weight gradients
 constexpr int kRowBlk = 128;                       // rows per quantization tile = rows per GEMM K stage
-constexpr int kQStride = 132;                      // LDS row stride (floats) of the 128 x 128 staging tile
-constexpr int kQLds = (kRowBlk * kQStride + 2 * kRowBlk) * 4;
+// Staging of a row block in LDS, as narrow as the values allow (more blocks per CU in flight): [dg | dv]
+// fp32; dy its bf16 bits; x and a their forward E4M3 codes plus one scale per row (the dequantized value
+// code * scale is formed again when read, the same fp32 product). Then an LDS copy of pblk (E <= 256).
+// [dg | dv] blocks take 32 channels of f and produce their 32 dg and 32 dv columns from one read of da,
+// g and v (64 output channels); the others take 128 channels (x and a are first quantized along 128
+// channels per row).
+template <int SRC>
+constexpr int wgrad_q_elem() { return SRC == kWgSrcDgv ? 4 : SRC == kWgSrcDy ? 2 : 1; }
+template <int SRC>
+constexpr int wgrad_q_cw() { return SRC == kWgSrcDgv ? 64 : 128; }
+template <int SRC>
+constexpr int wgrad_q_stride() { return wgrad_q_cw<SRC>() + 1; }   // odd: column reads spread over the banks
+template <int SRC>
+constexpr int wgrad_q_lds() {
+  return (kRowBlk * wgrad_q_stride<SRC>() * wgrad_q_elem<SRC>() + 3) / 4 * 4 + kRowBlk * 4 + 258 * 4;
+}
 
 // pblk[g] = first row block of group g (routed experts 0..E-1, then the shared block, empty unless
 // `shared`), pblk[E + 1] = their total: ceil(n_g / 128) blocks per group. One block, a scan over LDS.
@@ -148,36 +162,44 @@ __device__ __forceinline__ int wgrad_group_of(const int32_t* __restrict__ pblk, 
   return lo;
 }
 
-// One block per (row block b, 128-channel block): the block's rows are staged in LDS as fp32 (source
-// dependent, below), then every channel is quantized over the 128 rows and written transposed.
+// One block per (row block b, channel block): the block's rows are staged in LDS (source dependent,
+// below), then every channel is quantized over the 128 rows and written transposed.
 //   DY : dy rows (bf16) as given;
 //   X  : u rows (bf16, routed rows gathered through perm) -> 1x128 E4M3 along the channels, as the
 //        forward quantizes them, dequantized;
 //   A  : a = SiLU(g) * v from the fp32 [g | v] rows -> the forward's 1x128 requantization, dequantized;
-//   DGV: [dg | dv] from da and [g | v] (channels < fg: dg, else dv), fp32.
+//   DGV: dg and dv of 32 channels of f from da and [g | v], fp32 (output channels c and fg + c).
 template <int SRC>
 __global__ __launch_bounds__(256) void wgrad_quant_rows(WgQuantArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float qlds[];
-  float* tile = qlds;
-  float* red = qlds + kRowBlk * kQStride;          // [2][128] half-column maxima
+  extern __shared__ __attribute__((aligned(16))) uint8_t qlds[];
+  constexpr int kCW = wgrad_q_cw<SRC>(), kS = wgrad_q_stride<SRC>();
+  constexpr int kLPR = SRC == kWgSrcDgv ? 4 : kCW / 8, kRPP = 256 / kLPR;   // lanes per row, rows per pass
+  constexpr int kTileB = (kRowBlk * kS * wgrad_q_elem<SRC>() + 3) / 4 * 4;
+  float* rs = reinterpret_cast<float*>(qlds + kTileB);            // row scales (x, a)
+  int32_t* pb = reinterpret_cast<int32_t*>(qlds + kTileB + kRowBlk * 4);
   const int b = blockIdx.x, cb = blockIdx.y, tid = threadIdx.x;
   if (b >= a.pblk[a.E + 1]) return;
-  const int grp = wgrad_group_of(a.pblk, a.E, b);
+  // the group search runs on an LDS copy of the prefix (a search over global memory would wait for nine
+  // dependent loads)
+  for (int i = tid; i <= a.E + 1; i += 256) pb[i] = a.pblk[i];
+  __syncthreads();
+  const int grp = wgrad_group_of(pb, a.E, b);
   const bool shared = grp == a.E;
-  const int r0 = (b - a.pblk[grp]) * kRowBlk;
+  const int r0 = (b - pb[grp]) * kRowBlk;
   const int n = shared ? a.T : a.offsets[grp + 1] - a.offsets[grp];
   const int nrows = min(kRowBlk, n - r0);
   const int rowbase = (shared ? 0 : a.offsets[grp]) + r0;
-  const int c8 = (tid & 15) * 8;
-  for (int pass = 0; pass < kRowBlk / 16; ++pass) {
-    const int rr = pass * 16 + (tid >> 4);
+  const int c8 = (tid % kLPR) * 8;
+#pragma unroll 4
+  for (int pass = 0; pass < kRowBlk / kRPP; ++pass) {
+    const int rr = pass * kRPP + tid / kLPR;
     float v[8];
-    if (rr < nrows) {                              // uniform over the 16 lanes of a row
+    if (rr < nrows) {                              // uniform over the lanes of a row
       const int row = rowbase + rr;
       if constexpr (SRC == kWgSrcDy || SRC == kWgSrcX) {
         const uint16_t* base = shared ? a.bf_s : a.bf_r;
         const size_t srow = SRC == kWgSrcX && !shared ? (size_t)a.perm[row] : (size_t)row;
-        const uint4 raw = *reinterpret_cast<const uint4*>(base + srow * a.C + cb * 128 + c8);
+        const uint4 raw = *reinterpret_cast<const uint4*>(base + srow * a.C + cb * kCW + c8);
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -185,7 +207,7 @@ __global__ __launch_bounds__(256) void wgrad_quant_rows(WgQuantArgs a) {
           v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
       } else if constexpr (SRC == kWgSrcA) {
-        const float* gr = (shared ? a.gv_s : a.gv_r) + (size_t)row * 2 * a.fg + cb * 128 + c8;
+        const float* gr = (shared ? a.gv_s : a.gv_r) + (size_t)row * 2 * a.fg + cb * kCW + c8;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const float4 g4 = *reinterpret_cast<const float4*>(gr + 4 * h);
@@ -196,8 +218,7 @@ __global__ __launch_bounds__(256) void wgrad_quant_rows(WgQuantArgs a) {
           v[4 * h + 3] = silu(g4.w) * v4.w;
         }
       } else {
-        const bool up = cb * 128 >= a.fg;
-        const int c = cb * 128 - (up ? a.fg : 0) + c8;
+        const int c = cb * 32 + c8;
         const float* gr = (shared ? a.gv_s : a.gv_r) + (size_t)row * 2 * a.fg + c;
         const float* dr = (shared ? a.da_s : a.da_r) + (size_t)row * a.fg + c;
         float d8[8], g8[8], u8[8];
@@ -210,11 +231,13 @@ __global__ __launch_bounds__(256) void wgrad_quant_rows(WgQuantArgs a) {
           g8[4 * h] = y.x; g8[4 * h + 1] = y.y; g8[4 * h + 2] = y.z; g8[4 * h + 3] = y.w;
           u8[4 * h] = z.x; u8[4 * h + 1] = z.y; u8[4 * h + 2] = z.z; u8[4 * h + 3] = z.w;
         }
+        float* t = reinterpret_cast<float*>(qlds) + rr * kS + c8;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           float dg, dv;
           swiglu_grad(d8[k], g8[k], u8[k], dg, dv);
-          v[k] = up ? dv : dg;
+          t[k] = dg;
+          t[32 + k] = dv;
         }
       }
       if constexpr (SRC == kWgSrcX || SRC == kWgSrcA) {
@@ -225,48 +248,71 @@ __global__ __launch_bounds__(256) void wgrad_quant_rows(WgQuantArgs a) {
         for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
         float sc, inv;
         e4m3_scales(amax, sc, inv);
-        const int q0 = (int)f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-        const int q1 = (int)f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-        v[0] = __builtin_amdgcn_cvt_f32_fp8(q0, 0) * sc;
-        v[1] = __builtin_amdgcn_cvt_f32_fp8(q0, 1) * sc;
-        v[2] = __builtin_amdgcn_cvt_f32_fp8(q0, 2) * sc;
-        v[3] = __builtin_amdgcn_cvt_f32_fp8(q0, 3) * sc;
-        v[4] = __builtin_amdgcn_cvt_f32_fp8(q1, 0) * sc;
-        v[5] = __builtin_amdgcn_cvt_f32_fp8(q1, 1) * sc;
-        v[6] = __builtin_amdgcn_cvt_f32_fp8(q1, 2) * sc;
-        v[7] = __builtin_amdgcn_cvt_f32_fp8(q1, 3) * sc;
+        const uint32_t q0 = f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        const uint32_t q1 = f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+        uint8_t* t8 = qlds + rr * kS + c8;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          t8[k] = uint8_t(q0 >> (8 * k));
+          t8[4 + k] = uint8_t(q1 >> (8 * k));
+        }
+        if ((tid & 15) == 0) rs[rr] = sc;
+      } else if constexpr (SRC == kWgSrcDy) {
+        uint16_t* t16 = reinterpret_cast<uint16_t*>(qlds) + rr * kS + c8;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t16[k] = uint16_t(__float_as_uint(v[k]) >> 16);
       }
     } else {
+      // rows past the group's end are zero
+      if constexpr (SRC == kWgSrcX || SRC == kWgSrcA) {
+        uint8_t* t8 = qlds + rr * kS + c8;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = 0.f;
+        for (int k = 0; k < 8; ++k) t8[k] = 0;
+        if ((tid & 15) == 0) rs[rr] = 0.f;
+      } else if constexpr (SRC == kWgSrcDy) {
+        uint16_t* t16 = reinterpret_cast<uint16_t*>(qlds) + rr * kS + c8;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t16[k] = 0;
+      } else {
+        float* t = reinterpret_cast<float*>(qlds) + rr * kS + c8;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t[k] = t[32 + k] = 0.f;
+      }
     }
-    float* t = tile + rr * kQStride + c8;
-    *reinterpret_cast<float4*>(t) = float4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<float4*>(t + 4) = float4{v[4], v[5], v[6], v[7]};
   }
   __syncthreads();
-  // channel c, rows 64 h .. 64 h + 63
-  const int c = tid & 127, h = tid >> 7;
-  const float* col = tile + 64 * h * kQStride + c;
-  float amax = 0.f;
-  for (int r = 0; r < 64; ++r) amax = fmaxf(amax, fabsf(col[r * kQStride]));
-  red[h * kRowBlk + c] = amax;
-  __syncthreads();
-  amax = fmaxf(red[c], red[kRowBlk + c]);
-  float sc, inv;
-  e4m3_scales(amax, sc, inv);
-  uint8_t* q = a.qt + (size_t)(cb * 128 + c) * a.rpad + (size_t)b * kRowBlk + 64 * h;
+  // 8 lanes per channel, 16 consecutive rows each: one store instruction of a wave writes the whole
+  // 128-row run of 8 channels (8 full cache lines of the transposed output)
+  const int lane = tid & 63, wave = tid >> 6, sub = lane & 7, cl = lane >> 3;
+#pragma unroll 1
+  for (int pass = 0; pass < kCW / 32; ++pass) {
+    const int c = pass * 32 + wave * 8 + cl;
+    float v[16];
+    float amax = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+    for (int r = 0; r < 16; ++r) {
+      const int row = 16 * sub + r;
+      if constexpr (SRC == kWgSrcX || SRC == kWgSrcA)
+        v[r] = __builtin_amdgcn_cvt_f32_fp8((int)qlds[row * kS + c], 0) * rs[row];
+      else if constexpr (SRC == kWgSrcDy)
+        v[r] = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(qlds)[row * kS + c]) << 16);
+      else
+        v[r] = reinterpret_cast<const float*>(qlds)[row * kS + c];
+      amax = fmaxf(amax, fabsf(v[r]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    float sc, inv;
+    e4m3_scales(amax, sc, inv);
     uint32_t o[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float* e = col + (16 * w + 4 * k) * kQStride;
-      o[k] = f32x4_to_e4m3x4(e[0] * inv, e[kQStride] * inv, e[2 * kQStride] * inv, e[3 * kQStride] * inv);
-    }
-    *reinterpret_cast<uint4*>(q + 16 * w) = uint4{o[0], o[1], o[2], o[3]};
+    for (int k = 0; k < 4; ++k)
+      o[k] = f32x4_to_e4m3x4(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
+    const int gc = SRC == kWgSrcDgv ? (c < 32 ? cb * 32 + c : a.fg + cb * 32 + c - 32) : cb * kCW + c;
+    *reinterpret_cast<uint4*>(a.qt + (size_t)gc * a.rpad + (size_t)b * kRowBlk + 16 * sub) = uint4{o[0], o[1], o[2], o[3]};
+    if (sub == 0) a.st[(size_t)b * a.C + gc] = sc;
   }
-  if (h == 0) a.st[(size_t)b * a.C + cb * 128 + c] = sc;
 }
 
 // out[m][n] = sum over the group's row blocks kb of  sum_{k in kb} B[m][k] A[n][k] * sB[kb][m] sA[kb][n],
@@ -377,17 +423,18 @@ hipError_t launch_wgrad_quant(const WgQuantArgs& a, int src, int nblk_max, hipSt
                         (const void*)wgrad_quant_rows<kWgSrcA>, (const void*)wgrad_quant_rows<kWgSrcDgv>};
   if (src < 0 || src > 3) return hipErrorInvalidValue;
   if (nblk_max == 0) return hipSuccess;
+  const int ldsb[4] = {wgrad_q_lds<kWgSrcDy>(), wgrad_q_lds<kWgSrcX>(), wgrad_q_lds<kWgSrcA>(), wgrad_q_lds<kWgSrcDgv>()};
   if (!attr_done[src]) {
-    const hipError_t e = hipFuncSetAttribute(fns[src], hipFuncAttributeMaxDynamicSharedMemorySize, kQLds);
+    const hipError_t e = hipFuncSetAttribute(fns[src], hipFuncAttributeMaxDynamicSharedMemorySize, ldsb[src]);
     if (e != hipSuccess) return e;
     attr_done[src] = true;
   }
-  const dim3 grid(nblk_max, a.C / 128);
+  const dim3 grid(nblk_max, a.C / 128), grid64(nblk_max, a.C / 64);
   switch (src) {
-    case kWgSrcDy: wgrad_quant_rows<kWgSrcDy><<<grid, 256, kQLds, s>>>(a); break;
-    case kWgSrcX: wgrad_quant_rows<kWgSrcX><<<grid, 256, kQLds, s>>>(a); break;
-    case kWgSrcA: wgrad_quant_rows<kWgSrcA><<<grid, 256, kQLds, s>>>(a); break;
-    default: wgrad_quant_rows<kWgSrcDgv><<<grid, 256, kQLds, s>>>(a); break;
+    case kWgSrcDy: wgrad_quant_rows<kWgSrcDy><<<grid, 256, ldsb[0], s>>>(a); break;
+    case kWgSrcX: wgrad_quant_rows<kWgSrcX><<<grid, 256, ldsb[1], s>>>(a); break;
+    case kWgSrcA: wgrad_quant_rows<kWgSrcA><<<grid, 256, ldsb[2], s>>>(a); break;
+    default: wgrad_quant_rows<kWgSrcDgv><<<grid64, 256, ldsb[3], s>>>(a); break;
   }
   return hipGetLastError();
 }
