@@ -16,6 +16,8 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 namespace moe {
 
@@ -132,6 +134,7 @@ constexpr int wgrad_q_lds() {
 
 // pblk[g] = first row block of group g (routed experts 0..E-1, then the shared block, empty unless
 // `shared`), pblk[E + 1] = their total: ceil(n_g / 128) blocks per group. One block, a scan over LDS.
+// pblk[E + 2 .. E + 17] are cleared: the tile counters of the two weight-gradient GEMMs.
 __global__ __launch_bounds__(512) void wgrad_block_prefix(const int32_t* __restrict__ offsets, int E, int T,
                                                           int shared, int32_t* __restrict__ pblk) {
   __shared__ int buf[512];
@@ -149,6 +152,7 @@ __global__ __launch_bounds__(512) void wgrad_block_prefix(const int32_t* __restr
   }
   if (g <= E) pblk[g + 1] = buf[g];
   if (g == 0) pblk[0] = 0;
+  if (g < 16) pblk[E + 2 + g] = 0;   // the weight-gradient GEMMs' tile counters
 }
 
 // The group holding row block b: the last g with pblk[g] <= b (a non-empty group; b < pblk[E + 1]).
@@ -316,96 +320,263 @@ __global__ __launch_bounds__(256) void wgrad_quant_rows(WgQuantArgs a) {
 }
 
 // out[m][n] = sum over the group's row blocks kb of  sum_{k in kb} B[m][k] A[n][k] * sB[kb][m] sA[kb][n],
-// bf16, one 128 x 128 output tile per block (4 waves of 64 x 64). A is the MFMA A operand (output
-// columns, so a lane's four accumulators are four adjacent columns of one output row); each
-// 16x16x128 product is promoted with the product of its row's and its column's scales. Operands go
-// global -> LDS by LDS-DMA into one buffer (16-byte chunks XOR-swizzled by row), three blocks per CU
-// overlap each other's waits. Tiles of the shared block (the longest contraction) come first, then the
-// routed experts in order; inside a group the larger output dimension runs fastest, so the blocks of
-// an XCD (block id mod 8) share the smaller operand and split the larger one.
-__global__ __launch_bounds__(256, 3) void grouped_wgrad_mfma(WgGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kRowBlk * 128 + 2 * kRowBlk * 4];
-  uint8_t* sA = lds;
-  uint8_t* sB = lds + kRowBlk * 128;
-  float* sAs = reinterpret_cast<float*>(lds + 2 * kRowBlk * 128);
-  float* sBs = sAs + kRowBlk;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1, tr = lane & 15, g = lane >> 4;
-  const int mtn = a.M / 128, ntn = a.N / 128, tpg = mtn * ntn;
-  const int t = blockIdx.x;
-  const int gi = t / tpg, rem = t - gi * tpg;
-  const int group = a.shared ? (gi == 0 ? a.E : gi - 1) : gi;
-  int mt, nt;
-  if (a.M > a.N) {
-    nt = rem / mtn;
-    mt = rem - nt * mtn;
-  } else {
-    mt = rem / ntn;
-    nt = rem - mt * ntn;
+// bf16. One persistent block of 512 threads (8 waves, two per SIMD) per CU takes 256 x 256 output tiles;
+// the K dimension of a tile is its group's row blocks (128 rows = one 16x16x128 MFMA deep, promoted into
+// fp32 with the product of its row's and its column's scales). Both operands go global -> LDS by LDS-DMA
+// into a ring of two stages (16-byte chunks XOR-swizzled by row); the loader runs one stage ahead, also
+// across tile boundaries. Wave w multiplies output columns 64 (w mod 4).. and rows 128 (w div 4)..: A is
+// the MFMA A operand, so a lane's accumulators are output columns. The A rows of a stage are loaded in the
+// column order that gives each lane 8 adjacent columns of one output row per pair of 16-column MFMA
+// tiles, and a tile's bf16 result is stored during the next tile's first stage (its stores then complete
+// behind that stage's MFMAs). Tile list: the shared block first (the longest contraction), then the
+// routed experts; inside a group the output rows run fastest. The list is cut into eight ranges of equal
+// estimated cost (stages + 1 per tile), one per XCD (block id mod 8), whose blocks take tiles in order
+// from the XCD's counter. A tile of an empty group multiplies nothing and stores zeros.
+constexpr int kWgT = 256;
+constexpr int kWgThreads = 512;
+constexpr int kWgOp = kWgT * 128;                  // one operand of a stage: 256 rows x 128 bytes
+constexpr int kWgSlot = 2 * kWgOp + 2 * kWgT * 4;  // both operands + their scales
+constexpr int kWgIds = 2 * kWgSlot;                // ring of the block's next tile ids
+constexpr int kWgLds = kWgIds + 16;
+static_assert(kWgLds <= 160 * 1024, "LDS");
+
+// Output column (within a wave's 64) of A row l = 16 i + 4 g + r of the stage: a lane of group g holds, for
+// MFMA tiles 2p and 2p + 1, columns 32 p + 8 g + 0..7.
+__device__ __forceinline__ int wgrad_col_of(int l) {
+  const int i = l >> 4, g = (l >> 2) & 3, r = l & 3;
+  return 32 * (i >> 1) + 8 * g + 4 * (i & 1) + r;
+}
+
+__global__ __launch_bounds__(kWgThreads, 1) void grouped_wgrad_mfma(WgGemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 3, wm = wave >> 2, tr = lane & 15, g = lane >> 4;
+  const int E = a.E, M = a.M, N = a.N;
+  const bool has_shared = a.shared != 0;
+  const int G = E + (has_shared ? 1 : 0);
+  const int mtn = (M + kWgT - 1) / kWgT, ntn = (N + kWgT - 1) / kWgT, tpg = mtn * ntn;
+  const int32_t* pb = a.pblk;
+  const int S = pb[E + 1];
+  const int nks = has_shared ? S - pb[E] : 0;
+  // row blocks of the groups before position go of the tile list, and the group at that position
+  auto stages_before = [&](int go) { return has_shared ? (go == 0 ? 0 : nks + pb[go - 1]) : pb[go]; };
+  auto group_at = [&](int go) { return has_shared ? (go == 0 ? E : go - 1) : go; };
+  // first tile of XCD x's range: cost of the tiles before tile go * tpg + r is tpg (stages_before(go) + go)
+  // + r (stages of group go + 1)
+  auto range_start = [&](int x) {
+    if (x >= 8) return G * tpg;
+    const long long target = (long long)tpg * (S + G) * x / 8;
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((long long)tpg * (stages_before(mid) + mid) <= target) lo = mid;
+      else hi = mid;
+    }
+    const long long rem = target - (long long)tpg * (stages_before(lo) + lo);
+    const int c = stages_before(lo + 1) - stages_before(lo) + 1;
+    return lo * tpg + (int)min((rem + c - 1) / c, (long long)tpg);
+  };
+  const int xcd = blockIdx.x & 7;
+  const int t_begin = range_start(xcd), t_end = range_start(xcd + 1);
+  int32_t* ids = reinterpret_cast<int32_t*>(lds + kWgIds);
+  int pending = 0;
+  if (tid == 0) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) ids[k] = t_begin + atomicAdd(a.xcount + xcd, 1);
+    pending = t_begin + atomicAdd(a.xcount + xcd, 1);
   }
-  const int m0 = mt * 128, n0 = nt * 128;
-  const int kb0 = a.pblk[group], nk = a.pblk[group + 1] - kb0;
-  // copy geometry: piece 256 q + tid lands at LDS row (256 q + tid) / 8, position tid % 8, which holds
-  // global chunk (tid % 8) ^ (row & 7)
-  const int prow = tid >> 3, pchunk = ((tid & 7) ^ (prow & 7)) * 16;
-  const uint8_t* gA = a.A + (size_t)(n0 + prow) * a.rpad + pchunk;
-  const uint8_t* gB = a.B + (size_t)(m0 + prow) * a.rpad + pchunk;
-  f32x4 acc[4][4];
+  barrier_lds();
+  int id_l = __builtin_amdgcn_readfirstlane(ids[0]);
+  if (id_l >= t_end) return;
+  int ktile = 0;
+
+  // ---- loader. Thread tid moves, per stage and operand, the 16-byte pieces 512 q + tid (q < 4): LDS row
+  // 64 q + lrow, position tid % 8, which holds global chunk (tid % 8) ^ (lrow % 8). LDS A row 64 q + l is
+  // output column 64 q + wgrad_col_of(l) of the tile.
+  const int lrow = tid >> 3;
+  const int lchunk = ((tid & 7) ^ (lrow & 7)) * 16;
+  const int acol = wgrad_col_of(lrow);
+  struct Tile {
+    int group, m0, n0, kb0, nk;
+  };
+  auto decode = [&](int id) {
+    Tile t;
+    const int go = id / tpg, rem = id - go * tpg;
+    t.group = group_at(go);
+    const int nt = rem / mtn;
+    t.m0 = (rem - nt * mtn) * kWgT;
+    t.n0 = nt * kWgT;
+    t.kb0 = pb[t.group];
+    t.nk = pb[t.group + 1] - t.kb0;
+    return t;
+  };
+  Tile tl = decode(id_l);
+  // per tile: this thread's A and B row pointers for q = 0 (rows q = 1..3 follow at 64-row steps; in a tile
+  // that ends 128 rows early, rows past the end re-read the valid half) and its wave's scale pointer
+  const uint8_t* pA = nullptr;
+  const uint8_t* pB = nullptr;
+  const float* ps = nullptr;
+  int kl = 0, started = 1, nst_l = 1, a_half = 0, b_half = 0;
+  bool live = true;
+  auto setup = [&]() {
+    // an empty group re-reads row block 0 (never multiplied): its own start may lie past the last block
+    const int kb0 = tl.nk > 0 ? tl.kb0 : 0;
+    nst_l = max(tl.nk, 1);
+    a_half = tl.n0 + kWgT > N ? 2 : 4;   // q >= a_half: rows past the end
+    b_half = tl.m0 + kWgT > M ? 2 : 4;
+    pA = a.A + (size_t)(tl.n0 + acol) * a.rpad + (size_t)kb0 * 128 + lchunk;
+    pB = a.B + (size_t)(tl.m0 + lrow) * a.rpad + (size_t)kb0 * 128 + lchunk;
+    if (wave < 4) {
+      const int q = wave < a_half ? wave : wave - 2;
+      ps = a.As + (size_t)kb0 * N + tl.n0 + 64 * q + wgrad_col_of(lane);
+    } else {
+      // B scale position 128 h + 8 t + j holds row 128 h + 16 j + t: a lane reads its eight in one go
+      const int h = wave - 4 < b_half ? (wave - 4) >> 1 : 0;
+      const int pos = ((wave - 4) & 1) * 64 + lane;
+      ps = a.Bs + (size_t)kb0 * M + tl.m0 + 128 * h + 16 * (pos & 7) + (pos >> 3);
+    }
+    kl = 0;
+  };
+  setup();
+  auto issue = [&](uint8_t* sl) {
+    if (kl == nst_l && live) {
+      ++ktile;
+      id_l = __builtin_amdgcn_readfirstlane(ids[ktile & 3]);
+      if (id_l < t_end) {
+        tl = decode(id_l);
+        setup();
+        ++started;
+        // the id of tile ktile + 2 arrived a tile ago; request the one after it
+        if (tid == 0) {
+          ids[(ktile + 2) & 3] = pending;
+          pending = t_begin + atomicAdd(a.xcount + xcd, 1);
+        }
+      } else {
+        live = false;
+      }
+    }
+    const size_t kofs = (size_t)(live ? kl : 0) * 128;
+    ++kl;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 4; ++q)
+      dma16(pA + (size_t)(64 * (q < a_half ? q : q - 2)) * a.rpad + kofs, sl + (q * kWgThreads + wave * 64) * 16);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < 4; ++q)
+      dma16(pB + (size_t)(64 * (q < b_half ? q : q - 2)) * a.rpad + kofs, sl + kWgOp + (q * kWgThreads + wave * 64) * 16);
+    dma4(ps + (kofs / 128) * (wave < 4 ? N : M), sl + 2 * kWgOp + wave * 256);
+  };
+
   auto rd = [&](const uint8_t* base, int row) {
     const i32x4 lo = *reinterpret_cast<const i32x4*>(base + row * 128 + ((g ^ (row & 7)) * 16));
     const i32x4 hi = *reinterpret_cast<const i32x4*>(base + row * 128 + (((4 + g) ^ (row & 7)) * 16));
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  for (int s = 0; s < nk; ++s) {
-    const size_t kofs = (size_t)(kb0 + s) * kRowBlk;
+
+  // ---- compute: the tile being multiplied, and the bf16 result of the previous one awaiting its stores
+  Tile tc = tl;
+  int nst_c = nst_l, done = 0;
+  f32x4 acc[4][8];
+  uint4 res[8][2];
+  uint16_t* res_out = nullptr;   // this lane's first output of the pending result; null: nothing to store
+  // One stage: wait for its copies, start the next stage's, store the pending result (first stage of a
+  // tile), multiply. FIRST: the products initialise the accumulators.
+  auto stage = [&](int gs, auto first_tag) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    uint8_t* cur = lds + (gs & 1) * kWgSlot;
+    wait_vm0();       // this wave's copies of stage gs (and the previous stores) are done
+    barrier_lds();    // ... and every wave's; every wave is done with the other slot
+    issue(lds + ((gs + 1) & 1) * kWgSlot);
+    if constexpr (FIRST) {
+      if (res_out) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      dma16(gA + (size_t)(32 * q) * a.rpad + kofs, sA + (q * 256 + wave * 64) * 16);
-      dma16(gB + (size_t)(32 * q) * a.rpad + kofs, sB + (q * 256 + wave * 64) * 16);
-    }
-    if (wave < 2)
-      dma4(a.As + (size_t)(kb0 + s) * a.N + n0 + wave * 64 + lane, reinterpret_cast<uint8_t*>(sAs) + wave * 256);
-    else
-      dma4(a.Bs + (size_t)(kb0 + s) * a.M + m0 + (wave - 2) * 64 + lane, reinterpret_cast<uint8_t*>(sBs) + (wave - 2) * 256);
-    wait_vm0();
-    barrier_lds();
-    i32x8 aa[4];
-    f32x4 sa[4];
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      aa[i] = rd(sA, 64 * wn + 16 * i + tr);
-      sa[i] = *reinterpret_cast<const f32x4*>(sAs + 64 * wn + 16 * i + 4 * g);
-    }
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const i32x8 bb = rd(sB, 64 * wm + 16 * j + tr);
-      const float sb = sBs[64 * wm + 16 * j + tr];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa[i], bb, zero, 0, 0, 0, 127, 0, 127);
-        acc[i][j] += (sa[i] * sb) * p;
+          for (int p = 0; p < 2; ++p) *reinterpret_cast<uint4*>(res_out + (size_t)(16 * j) * N + 32 * p) = res[j][p];
       }
     }
-    barrier_lds();   // every wave is done with the buffer before the next stage's copies land in it
-  }
-  uint16_t* out = (group == a.E ? a.out_s : a.out_r + (size_t)group * a.M * a.N);
+    const bool active = tc.nk > 0 && tc.n0 + 64 * wn < N && tc.m0 + 128 * wm < M;
+    if (active) {
+      const uint8_t* sA = cur;
+      const uint8_t* sB = cur + kWgOp;
+      const float* sAs = reinterpret_cast<const float*>(cur + 2 * kWgOp);
+      const float* sBs = sAs + kWgT;
+      i32x8 aa[4];
+      f32x4 sa[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + 64 * wm + 16 * j + tr;
+      for (int i = 0; i < 4; ++i) {
+        aa[i] = rd(sA, 64 * wn + 16 * i + tr);
+        sa[i] = *reinterpret_cast<const f32x4*>(sAs + 64 * wn + 16 * i + 4 * g);
+      }
+      // the B rows and scales of the next 16-row tile load while the current one multiplies; each product
+      // is promoted one MFMA after it is issued, so the matrix core and the vector ALU overlap
+      i32x8 bb[2];
+      const f32x4 sb0 = *reinterpret_cast<const f32x4*>(sBs + 128 * wm + 8 * tr);
+      const f32x4 sb1 = *reinterpret_cast<const f32x4*>(sBs + 128 * wm + 8 * tr + 4);
+      const float sbv[8] = {sb0[0], sb0[1], sb0[2], sb0[3], sb1[0], sb1[1], sb1[2], sb1[3]};
+      bb[0] = rd(sB, 128 * wm + tr);
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      f32x4 pr[2], cs[4];
+      auto promote = [&](int i, int j, const f32x4& p, const f32x4& c) {
+        if constexpr (FIRST) acc[i][j] = c * p;
+        else acc[i][j] += c * p;
+      };
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        ([&] {
+          constexpr int j = J;
+          if constexpr (j + 1 < 8) bb[(j + 1) & 1] = rd(sB, 128 * wm + 16 * (j + 1) + tr);
+          [&]<int... I>(std::integer_sequence<int, I...>) {
+            ([&] {
+              constexpr int i = I;
+              pr[i & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa[i], bb[j & 1], zero, 0, 0, 0, 127, 0, 127);
+              if constexpr (i > 0) promote(i - 1, j, pr[(i - 1) & 1], cs[i - 1]);
+              else if constexpr (j > 0) promote(3, j - 1, pr[1], cs[3]);
+              cs[i] = sa[i] * sbv[j];
+            }(), ...);
+          }(std::make_integer_sequence<int, 4>{});
+        }(), ...);
+      }(std::make_integer_sequence<int, 8>{});
+      promote(3, 7, pr[1], cs[3]);
+    } else if constexpr (FIRST) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n0 + 64 * wn + 16 * i + 4 * g;
-      uint2 v;
-      v.x = uint32_t(f32_to_bf16(acc[i][j][0])) | (uint32_t(f32_to_bf16(acc[i][j][1])) << 16);
-      v.y = uint32_t(f32_to_bf16(acc[i][j][2])) | (uint32_t(f32_to_bf16(acc[i][j][3])) << 16);
-      *reinterpret_cast<uint2*>(out + (size_t)m * a.N + n) = v;
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+
+  issue(lds);
+  for (int gs = 0;;) {
+    stage(gs++, std::true_type{});
+    for (int kb = 1; kb < nst_c; ++kb) stage(gs++, std::false_type{});
+
+    // ---- tile tc is complete: lane holds, for output row m0 + 128 wm + 16 j + tr, columns
+    // n0 + 64 wn + 32 p + 8 g + 0..7 in acc[2p][j], acc[2p + 1][j]
+    const bool valid = tc.n0 + 64 * wn < N && tc.m0 + 128 * wm < M;
+    uint16_t* out = tc.group == E ? a.out_s : a.out_r + (size_t)tc.group * M * N;
+    res_out = valid ? out + (size_t)(tc.m0 + 128 * wm + tr) * N + tc.n0 + 64 * wn + 8 * g : nullptr;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const f32x4 x = acc[2 * p][j], y = acc[2 * p + 1][j];
+        res[j][p] = uint4{uint32_t(f32_to_bf16(x[0])) | (uint32_t(f32_to_bf16(x[1])) << 16),
+                          uint32_t(f32_to_bf16(x[2])) | (uint32_t(f32_to_bf16(x[3])) << 16),
+                          uint32_t(f32_to_bf16(y[0])) | (uint32_t(f32_to_bf16(y[1])) << 16),
+                          uint32_t(f32_to_bf16(y[2])) | (uint32_t(f32_to_bf16(y[3])) << 16)};
+      }
+    if (++done == started && !live) break;
+    // the loader moved to this tile while the last stage of the previous one was multiplied
+    tc = tl;
+    nst_c = nst_l;
   }
+  if (res_out) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) *reinterpret_cast<uint4*>(res_out + (size_t)(16 * j) * N + 32 * p) = res[j][p];
+  }
+  wait_vm0();
 }
 
 int wgrad_row_blocks_max(int T, int K, int E, bool shared) {
@@ -439,10 +610,14 @@ hipError_t launch_wgrad_quant(const WgQuantArgs& a, int src, int nblk_max, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_wgrad_gemm(const WgGemmArgs& a, hipStream_t s) {
-  const long long tiles = (long long)(a.E + (a.shared ? 1 : 0)) * (a.M / 128) * (a.N / 128);
-  if (tiles == 0) return hipSuccess;
-  grouped_wgrad_mfma<<<(unsigned)tiles, 256, 0, s>>>(a);
+hipError_t launch_wgrad_gemm(const WgGemmArgs& a, int grid, hipStream_t s) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    const hipError_t e = hipFuncSetAttribute((const void*)grouped_wgrad_mfma, hipFuncAttributeMaxDynamicSharedMemorySize, kWgLds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  grouped_wgrad_mfma<<<grid, kWgThreads, kWgLds, s>>>(a);
   return hipGetLastError();
 }
 

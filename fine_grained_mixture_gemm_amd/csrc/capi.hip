@@ -221,7 +221,7 @@ BwdLayout bwd_layout(const moe_config* c) {
   L.nblk = wgrad_row_blocks_max(c->T, c->top_k, c->n_routed, fs > 0);
   L.rpad = (size_t)L.nblk * 128;
   const size_t nb = L.nblk;
-  L.pblk = take((E + 2) * 4);
+  L.pblk = take((E + 2 + 16) * 4);
   L.wq_dy = take(d * L.rpad);
   L.ws_dy = take(nb * d * 4);
   L.wq_a = take(f * L.rpad);
@@ -291,7 +291,9 @@ moe_status weight_gradients(const moe_config* c, const BwdLayout& L, uint8_t* ba
   g.Bs = F(L.ws_dy);
   g.out_r = static_cast<uint16_t*>(dw2);
   g.out_s = static_cast<uint16_t*>(dws2);
-  MOE_TRY(hip_status(launch_wgrad_gemm(g, s), "dW2 GEMM launch"));
+  g.xcount = pblk + E + 2;
+  const int grid = std::max(8, device_cus());
+  MOE_TRY(hip_status(launch_wgrad_gemm(g, grid, s), "dW2 GEMM launch"));
   // d[W1; W3] [2f][d]: rows from [dg | dv], columns from x
   g.M = 2 * f;
   g.N = d;
@@ -301,7 +303,8 @@ moe_status weight_gradients(const moe_config* c, const BwdLayout& L, uint8_t* ba
   g.Bs = F(L.ws_dgv);
   g.out_r = static_cast<uint16_t*>(dw13);
   g.out_s = static_cast<uint16_t*>(dws13);
-  MOE_TRY(hip_status(launch_wgrad_gemm(g, s), "dW13 GEMM launch"));
+  g.xcount = pblk + E + 10;
+  MOE_TRY(hip_status(launch_wgrad_gemm(g, grid, s), "dW13 GEMM launch"));
   return MOE_OK;
 }
 

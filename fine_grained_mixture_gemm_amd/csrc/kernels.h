@@ -132,6 +132,7 @@ struct WgQuantArgs {
 };
 struct WgGemmArgs {
   const int32_t* pblk;
+  int32_t* xcount;            // 8 tile counters (one per XCD), zero at launch
   int E, shared, M, N;        // output [M][N] per group (multiples of 128)
   const uint8_t* A;           // [N][rpad] codes, scales As [row block][N]
   const float* As;
@@ -142,9 +143,10 @@ struct WgGemmArgs {
   uint16_t* out_s;            // bf16 [M][N]
 };
 int wgrad_row_blocks_max(int T, int K, int E, bool shared);
+// pblk[0..E+1], then 16 zeroed tile counters (two launches of the weight-gradient GEMM)
 hipError_t launch_wgrad_prefix(const int32_t* offsets, int E, int T, bool shared, int32_t* pblk, hipStream_t s);
 hipError_t launch_wgrad_quant(const WgQuantArgs& a, int src, int nblk_max, hipStream_t s);
-hipError_t launch_wgrad_gemm(const WgGemmArgs& a, hipStream_t s);
+hipError_t launch_wgrad_gemm(const WgGemmArgs& a, int grid, hipStream_t s);   // grid >= 8 (one block per CU)
 int balance_chunks_for(int T);
 int balance_sequences_max(int T);   // sequences of T tokens when seq_len is T or a multiple of 64
 hipError_t launch_balance_stats(const BalanceArgs& a, hipStream_t s);
