@@ -121,7 +121,7 @@ Layout layout(const moe_config* c) {
   const bool fp8 = c->w_dtype == MOE_FP8_E4M3;
   const size_t esz_a = c->w_dtype == MOE_F32 ? 4 : (c->w_dtype == MOE_BF16 ? 2 : 1);
   L.z = take(T * E * 4);
-  L.z64 = take(T * E * 8);
+  L.z64 = take(T * E * 8);   // also the MFMA logits' two fp32 partial slices
   L.wg_split = take(use_mfma_router(c) ? 3 * E * d * 2 : 0);
   int klen = 0;
   const int ksplit = use_mfma_router(c) ? 1 : router_ksplit((int)T, (int)E, (int)d, klen);

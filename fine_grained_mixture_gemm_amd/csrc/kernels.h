@@ -16,7 +16,8 @@ struct RouteArgs {
   int n_groups, topk_groups;   // group-limited routing (0: none)
   float delta;
   float* z;               // [T, E] fp32 logits
-  double* z64;            // [T, E] fp64 logits of rechecked tokens (compacted)
+  double* z64;            // [T, E] fp64 logits of rechecked tokens (compacted); MFMA logits: first the
+                          // fp32 partial sums of two slices of d
   uint16_t* wg_split;     // [3, E, d] bf16 parts of w_gate (MFMA logits)
   double* zpart;          // [ksplit, T, E] fp64 partial logits over slices of d (vector-ALU logits)
   int ksplit, klen;       // slices of d and their length (a multiple of 32); ksplit 1 writes z directly
@@ -25,6 +26,13 @@ struct RouteArgs {
   int32_t* topk_idx;
   float* topk_w;
 };
+
+// Slices of d for the MFMA router logits: two when one slice gives fewer than two 128 x 64 blocks per CU
+// (the chip's 256), each slice at least 8 stages of 64 (three slices measured slower than two).
+inline int router_mfma_slices(int T, int E, int d) {
+  const long long blocks = (long long)((T + 127) / 128) * ((E + 63) / 64);
+  return (blocks > 0 && blocks < 512 && d / 64 >= 16) ? 2 : 1;
+}
 
 // Slices of d for the vector-ALU router logits: enough 64x64 blocks to cover the chip when T and E are
 // small (a decode step), each slice at least 128 long, partial sums at most 64 MiB. Sets klen.

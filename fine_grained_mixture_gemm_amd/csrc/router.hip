@@ -102,29 +102,32 @@ __global__ __launch_bounds__(256) void router_split_wg(const float* __restrict__
 
 // 128 tokens x 64 experts per block; wave w owns experts 16w..16w+15 against all 128 tokens.
 // Tokens are staged 64 elements (128 bytes) at a time in a double-buffered XOR-swizzled LDS tile;
-// the centroid parts stream from global memory into registers.
+// the centroid parts stream from global memory into registers. blockIdx.z takes the slice
+// [z klen, (z + 1) klen) of d: with one slice the kernel writes z = sum + off, with several it writes
+// the slice's fp32 partial sum to zpart[z] and router_logits_sum32 adds the slices in order.
 __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ u, const uint16_t* __restrict__ parts,
                                                           const float* __restrict__ off, int T, int E, int d,
-                                                          float* __restrict__ z, int* __restrict__ recheck_count) {
+                                                          int klen, float* __restrict__ z, float* __restrict__ zpart,
+                                                          int* __restrict__ recheck_count) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][128 * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * 128, e0 = blockIdx.y * 64;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *recheck_count = 0;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *recheck_count = 0;
   const size_t n = (size_t)E * d;
+  const int s0 = blockIdx.z * (klen / 64), nst = min(d, (int)(blockIdx.z + 1) * klen) / 64 - s0;
   const int erow = min(e0 + 16 * wave + (lane & 15), E - 1);
-  const uint8_t* wp = reinterpret_cast<const uint8_t*>(parts + (size_t)erow * d) + 16 * (lane >> 4);
+  const uint8_t* wp = reinterpret_cast<const uint8_t*>(parts + (size_t)erow * d) + 16 * (lane >> 4) + 128 * s0;
   const uint8_t* ub = reinterpret_cast<const uint8_t*>(u);
   uint32_t boff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int id16 = q * 256 + tid;
     const int tok = min(t0 + (id16 >> 3), T - 1);
-    boff[q] = (uint32_t)tok * (uint32_t)d * 2u + (id16 & 7) * 16;
+    boff[q] = (uint32_t)tok * (uint32_t)d * 2u + (id16 & 7) * 16 + 128u * s0;
   }
   f32x4 acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nst = d / 64;
   i32x4 Bst[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) Bst[q] = *reinterpret_cast<const i32x4*>(ub + boff[q]);
@@ -186,16 +189,40 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int e = e0 + 16 * wave + 4 * (lane >> 4) + r;
-      if (e < E) z[(size_t)t * E + e] = acc[j][r] + (off ? off[e] : 0.f);
+      if (e >= E) continue;
+      if (zpart) zpart[((size_t)blockIdx.z * T + t) * E + e] = acc[j][r];
+      else z[(size_t)t * E + e] = acc[j][r] + (off ? off[e] : 0.f);
     }
+  }
+}
+
+// z[t, e] = fp32(sum over slices s = 0.. of zpart[s, t, e], in order) + off[e].
+__global__ __launch_bounds__(256) void router_logits_sum32(const float* __restrict__ zpart, int ks, int T, int E,
+                                                           const float* __restrict__ off, float* __restrict__ z) {
+  const size_t n = (size_t)T * E;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    float acc = zpart[i];
+    for (int k = 1; k < ks; ++k) acc += zpart[(size_t)k * n + i];
+    z[i] = acc + (off ? off[i % E] : 0.f);
   }
 }
 
 void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s) {
   const long long n = (long long)a.E * a.d;
   router_split_wg<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.wg, n, a.wg_split);
-  dim3 grid(cdiv(a.T, 128), cdiv(a.E, 64));
-  router_logits_mfma<<<grid, 256, 0, s>>>((const uint16_t*)a.u, a.wg_split, a.off, a.T, a.E, a.d, a.z, a.recheck_count);
+  // two slices of d when one gives fewer than two blocks per CU; their fp32 partial sums live in the
+  // space of the fp64 recheck logits, which are written only later
+  const int ks = router_mfma_slices(a.T, a.E, a.d);
+  const int klen = cdiv(a.d / 64, ks) * 64;
+  float* zp = ks > 1 ? reinterpret_cast<float*>(a.z64) : nullptr;
+  dim3 grid(cdiv(a.T, 128), cdiv(a.E, 64), ks);
+  router_logits_mfma<<<grid, 256, 0, s>>>((const uint16_t*)a.u, a.wg_split, a.off, a.T, a.E, a.d, klen, a.z, zp,
+                                          a.recheck_count);
+  if (ks > 1) {
+    const long long nz = (long long)a.T * a.E;
+    const long long nb = (nz + 255) / 256;
+    router_logits_sum32<<<(unsigned)(nb < 2048 ? nb : 2048), 256, 0, s>>>(zp, ks, a.T, a.E, a.off, a.z);
+  }
 }
 
 // ------------------------------------------------------------------ top-K of one token per wave
