@@ -11,6 +11,8 @@
 
 namespace moe {
 
+constexpr int kCombineMaxK = 8;   // routed rows held in registers at once (bf16 expert outputs)
+
 // BF16: u and h are bf16 (else fp32); YBF16: the expert outputs are bf16 (else fp32).
 template <bool BF16, bool YBF16>
 __global__ __launch_bounds__(256) void combine_rows(const void* __restrict__ u_, const void* __restrict__ yr_,
@@ -55,11 +57,31 @@ __global__ __launch_bounds__(256) void combine_rows(const void* __restrict__ u_,
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += y[i];
     }
-    for (int k = 0; k < K; ++k) {
-      load8(yr_, YBF16, (size_t)s_row[k] * d + col, y);
-      const float g = s_g[k];
+    if (YBF16 && K <= kCombineMaxK) {
+      // every routed row's piece is requested before the first is used (K loads in flight), then the
+      // rows are added in order
+      uint4 raw[kCombineMaxK];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, y[i], acc[i]);
+      for (int k = 0; k < kCombineMaxK; ++k)
+        if (k < K) raw[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(yr_) + (size_t)s_row[k] * d + col);
+#pragma unroll
+      for (int k = 0; k < kCombineMaxK; ++k) {
+        if (k >= K) break;
+        const float g = s_g[k];
+        const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(g, __uint_as_float(w[i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(g, __uint_as_float(w[i] & 0xFFFF0000u), acc[2 * i + 1]);
+        }
+      }
+    } else {
+      for (int k = 0; k < K; ++k) {
+        load8(yr_, YBF16, (size_t)s_row[k] * d + col, y);
+        const float g = s_g[k];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, y[i], acc[i]);
+      }
     }
     if constexpr (BF16) {
       uint4 o;
