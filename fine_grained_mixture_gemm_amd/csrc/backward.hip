@@ -15,6 +15,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <atomic>
+
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -589,16 +591,16 @@ hipError_t launch_wgrad_prefix(const int32_t* offsets, int E, int T, bool shared
 }
 
 hipError_t launch_wgrad_quant(const WgQuantArgs& a, int src, int nblk_max, hipStream_t s) {
-  static bool attr_done[4] = {false, false, false, false};
+  static std::atomic<bool> attr_done[4];   // set once per kernel (setting it twice is harmless)
   const void* fns[4] = {(const void*)wgrad_quant_rows<kWgSrcDy>, (const void*)wgrad_quant_rows<kWgSrcX>,
                         (const void*)wgrad_quant_rows<kWgSrcA>, (const void*)wgrad_quant_rows<kWgSrcDgv>};
   if (src < 0 || src > 3) return hipErrorInvalidValue;
   if (nblk_max == 0) return hipSuccess;
   const int ldsb[4] = {wgrad_q_lds<kWgSrcDy>(), wgrad_q_lds<kWgSrcX>(), wgrad_q_lds<kWgSrcA>(), wgrad_q_lds<kWgSrcDgv>()};
-  if (!attr_done[src]) {
+  if (!attr_done[src].load(std::memory_order_relaxed)) {
     const hipError_t e = hipFuncSetAttribute(fns[src], hipFuncAttributeMaxDynamicSharedMemorySize, ldsb[src]);
     if (e != hipSuccess) return e;
-    attr_done[src] = true;
+    attr_done[src].store(true, std::memory_order_relaxed);
   }
   const dim3 grid(nblk_max, a.C / 128), grid64(nblk_max, a.C / 64);
   switch (src) {
@@ -611,11 +613,11 @@ hipError_t launch_wgrad_quant(const WgQuantArgs& a, int src, int nblk_max, hipSt
 }
 
 hipError_t launch_wgrad_gemm(const WgGemmArgs& a, int grid, hipStream_t s) {
-  static bool attr_done = false;
-  if (!attr_done) {
+  static std::atomic<bool> attr_done{false};   // set once (setting it twice is harmless)
+  if (!attr_done.load(std::memory_order_relaxed)) {
     const hipError_t e = hipFuncSetAttribute((const void*)grouped_wgrad_mfma, hipFuncAttributeMaxDynamicSharedMemorySize, kWgLds);
     if (e != hipSuccess) return e;
-    attr_done = true;
+    attr_done.store(true, std::memory_order_relaxed);
   }
   grouped_wgrad_mfma<<<grid, kWgThreads, kWgLds, s>>>(a);
   return hipGetLastError();

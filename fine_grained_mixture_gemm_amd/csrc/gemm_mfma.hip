@@ -28,6 +28,8 @@
 // range of the tile list, in which neighbouring tiles share an expert's weight tile in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
+
+#include <atomic>
 #include "tiles.h"
 
 #include <utility>
@@ -458,15 +460,15 @@ int gemm_mfma_bm() { return kBM; }
 
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s, bool raw) {
   if (raw && !fp8) return hipErrorInvalidValue;
-  static bool attr_done[6] = {false, false, false, false, false, false};
+  static std::atomic<bool> attr_done[6];   // set once per kernel (setting it twice is harmless)
   const int k = raw ? 4 + (gateup ? 1 : 0) : (fp8 ? 2 : 0) + (gateup ? 1 : 0);
   const void* fns[6] = {(const void*)grouped_gemm_mfma<false, false>, (const void*)grouped_gemm_mfma<false, true>,
                         (const void*)grouped_gemm_mfma<true, false>, (const void*)grouped_gemm_mfma<true, true>,
                         (const void*)grouped_gemm_mfma<true, false, true>, (const void*)grouped_gemm_mfma<true, true, true>};
-  if (!attr_done[k]) {
+  if (!attr_done[k].load(std::memory_order_relaxed)) {
     hipError_t e = hipFuncSetAttribute(fns[k], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
-    attr_done[k] = true;
+    attr_done[k].store(true, std::memory_order_relaxed);
   }
   switch (k) {
     case 0: grouped_gemm_mfma<false, false><<<grid, kThreads, kLdsBytes, s>>>(a); break;
