@@ -36,6 +36,11 @@ SMALL = {
                                             topk_groups=4),
     "f32_sigmoid_norenorm": W["tiny_f32"].replace(name="f32_sigmoid_norenorm", gate="sigmoid_bias", renorm=False,
                                                   bias_range=0.1, T=77, E=9, K=3),
+    # more routed rows per token than the combine holds in registers at once (bf16 outputs), and the
+    # largest top-K the library takes
+    "bf16_k12": W["dsmoe2b_bf16"].replace(name="bf16_k12", T=150, d=256, E=24, K=12, f=128),
+    "bf16_k16_sigmoid": W["dsmoe2b_bf16"].replace(name="bf16_k16_sigmoid", T=90, d=256, E=20, K=16, f=128,
+                                                   gate="sigmoid_bias", renorm=True, bias_range=0.1, zipf=None),
 }
 
 
