@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_fp8")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload's layer with this many tokens instead (a sweep over batch sizes; the "
+                         "workload name gains a _t<T> suffix and no profiled traffic is attached)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the E4M3 expert backward")
     ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens of the workload the oracle runs")
@@ -277,6 +280,8 @@ def main():
     from synth import configs
 
     w = configs.WORKLOADS[args.workload]
+    if args.tokens > 0:
+        w = w.replace(name=f"{w.name}_t{args.tokens}", T=args.tokens)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)

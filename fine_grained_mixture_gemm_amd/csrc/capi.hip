@@ -48,8 +48,11 @@ constexpr float kRecheckDeltaSigmoid = 4e-5f;
 constexpr float kRecheckDeltaSoftmax = 2e-4f;
 
 bool use_mfma_gemm(const moe_config* c) { return c->w_dtype != MOE_F32; }
+// bf16 tokens take the MFMA logits from T * E >= 2^17 (512 tokens of 256 experts); below that the
+// vector-ALU logits split over d are faster (a decode step)
+constexpr long long kMfmaRouterMin = 1LL << 17;
 bool use_mfma_router(const moe_config* c) {
-  return c->act_dtype == MOE_BF16 && c->d_model % 64 == 0 && (long long)c->T * c->n_routed >= (1LL << 20);
+  return c->act_dtype == MOE_BF16 && c->d_model % 64 == 0 && (long long)c->T * c->n_routed >= kMfmaRouterMin;
 }
 
 // expert outputs: bf16 for E4M3 experts (the combine payload), fp32 otherwise
@@ -121,7 +124,7 @@ Layout layout(const moe_config* c) {
   const bool fp8 = c->w_dtype == MOE_FP8_E4M3;
   const size_t esz_a = c->w_dtype == MOE_F32 ? 4 : (c->w_dtype == MOE_BF16 ? 2 : 1);
   L.z = take(T * E * 4);
-  L.z64 = take(T * E * 8);   // also the MFMA logits' two fp32 partial slices
+  L.z64 = take(T * E * (use_mfma_router(c) ? 16 : 8));   // MFMA logits: also up to four fp32 partial slices
   L.wg_split = take(use_mfma_router(c) ? 3 * E * d * 2 : 0);
   int klen = 0;
   const int ksplit = use_mfma_router(c) ? 1 : router_ksplit((int)T, (int)E, (int)d, klen);

@@ -17,7 +17,7 @@ struct RouteArgs {
   float delta;
   float* z;               // [T, E] fp32 logits
   double* z64;            // [T, E] fp64 logits of rechecked tokens (compacted); MFMA logits: first the
-                          // fp32 partial sums of two slices of d
+                          // fp32 partial sums of up to four slices of d ([T, E] x 16 bytes)
   uint16_t* wg_split;     // [3, E, d] bf16 parts of w_gate (MFMA logits)
   double* zpart;          // [ksplit, T, E] fp64 partial logits over slices of d (vector-ALU logits)
   int ksplit, klen;       // slices of d and their length (a multiple of 32); ksplit 1 writes z directly
@@ -27,11 +27,16 @@ struct RouteArgs {
   float* topk_w;
 };
 
-// Slices of d for the MFMA router logits: two when one slice gives fewer than two 128 x 64 blocks per CU
-// (the chip's 256), each slice at least 8 stages of 64 (three slices measured slower than two).
+// Slices of d for the MFMA router logits: enough for about 512 blocks of 128 tokens x 64 experts (two
+// per CU of the chip's 256) when one slice gives fewer, at most four, each slice at least 8 stages of
+// 64 (at the V3 shape, 256 blocks: two slices; three slices there measured slower than two).
 inline int router_mfma_slices(int T, int E, int d) {
   const long long blocks = (long long)((T + 127) / 128) * ((E + 63) / 64);
-  return (blocks > 0 && blocks < 512 && d / 64 >= 16) ? 2 : 1;
+  if (blocks <= 0) return 1;
+  long long ks = 512 / blocks;
+  ks = ks < 1 ? 1 : (ks > 4 ? 4 : ks);
+  while (ks > 1 && d / 64 < 8 * ks) --ks;
+  return (int)ks;
 }
 
 // Slices of d for the vector-ALU router logits: enough 64x64 blocks to cover the chip when T and E are

@@ -210,8 +210,8 @@ __global__ __launch_bounds__(256) void router_logits_sum32(const float* __restri
 void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s) {
   const long long n = (long long)a.E * a.d;
   router_split_wg<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.wg, n, a.wg_split);
-  // two slices of d when one gives fewer than two blocks per CU; their fp32 partial sums live in the
-  // space of the fp64 recheck logits, which are written only later
+  // several slices of d when one gives fewer than two blocks per CU; their fp32 partial sums live in the
+  // space of the fp64 recheck logits (sized for four slices), which are written only later
   const int ks = router_mfma_slices(a.T, a.E, a.d);
   const int klen = cdiv(a.d / 64, ks) * 64;
   float* zp = ks > 1 ? reinterpret_cast<float*>(a.z64) : nullptr;
