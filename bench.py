@@ -90,7 +90,7 @@ def gateup_kernel_name(w):
     """The kernel that runs the gate/up projection of workload w (the library picks it from the config)."""
     if w.wdt == "f32":
         return "grouped_gemm_simt gate/up"
-    if w.wdt == "fp8" and w.T <= 64:
+    if w.wdt == "fp8" and w.T <= 128:
         return "grouped_gemm_decode gate/up+SwiGLU"
     return "grouped_gemm_mfma gate/up+SwiGLU"
 

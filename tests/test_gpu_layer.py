@@ -24,11 +24,13 @@ SMALL = {
     "fp8_sigmoid_ragged": W["v3_fp8"].replace(name="fp8_sigmoid_ragged", T=333, d=512, E=20, K=4),
     "fp8_k_equals_e": W["v3_fp8"].replace(name="fp8_k_equals_e", T=70, d=256, E=4, K=4),
     "fp8_one_token": W["v3_fp8"].replace(name="fp8_one_token", T=1, d=256, E=32, K=8),
-    # batches of at most 64 tokens take the E4M3 decode kernels: groups spanning 3 and 4 token tiles,
+    # batches of at most 128 tokens take the E4M3 decode kernels: groups spanning 3 and 4 token tiles,
     # two shared experts (shared inner dim 2 f)
     "fp8_decode_3tiles": W["v3_fp8"].replace(name="fp8_decode_3tiles", T=64, d=512, E=6, K=4),
     "fp8_decode_2shared": W["v3_fp8"].replace(name="fp8_decode_2shared", T=40, d=512, E=16, Ks=2, K=6),
     "fp8_decode_k_equals_e": W["v3_fp8"].replace(name="fp8_decode_k_equals_e", T=64, d=256, E=4, K=4),
+    # the largest decode batch: the shared group takes eight 16-token passes, routed groups several
+    "fp8_decode_128": W["v3_fp8"].replace(name="fp8_decode_128", T=128, d=512, E=16, K=4),
     # group-limited routing: 4 groups of 4 keeping 2 (softmax), 8 groups of 4 keeping 4 (sigmoid + bias)
     "bf16_group_limited": W["dsmoe2b_bf16"].replace(name="bf16_group_limited", T=300, d=256, E=16, K=3, f=128,
                                                      n_groups=4, topk_groups=2),
