@@ -316,8 +316,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
       dma16(Wk + (size_t)(wrow + lrow) * kbytes_l, sl + (q * kThreads + wave * 64) * 16);
     }
     const uint8_t* Xk = Xl + (size_t)kk * kStageB;
+    // 64-row groups of the token tile past its last row are not copied: their LDS rows keep older data,
+    // which only ever reaches the accumulators of padding tokens (a token's products use its own row
+    // only), and those are never stored
 #pragma unroll
-    for (int q = 0; q < kChunks; ++q) dma16(Xk + boff[q], sl + kSlotA + (q * kThreads + wave * 64) * 16);
+    for (int q = 0; q < kChunks; ++q)
+      if (q == 0 || 64 * q < tl.nrows) dma16(Xk + boff[q], sl + kSlotA + (q * kThreads + wave * 64) * 16);
     if (FP8 && wave < 4) dma4(XSl + sxoff + kk, sl + kSX + wave * 256);
     if (FP8 && wave == 4 && lane < 2) dma4(WSl + kk, sl + kWS);
   };
