@@ -33,9 +33,10 @@ hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_pr
 
 // Schedule of the matrix-core grouped GEMMs. The tile list (routed experts ascending, M index fastest
 // within an N tile, then the shared group) is cut into eight contiguous ranges of equal estimated
-// cost, one per XCD; a tile costs 10 when more than half of its bm rows are valid (both token halves
-// of the block multiply) and 7 otherwise (one half multiplies; streaming its weights still takes most
-// of the time). Within a range the blocks of that XCD take tiles in order from a counter.
+// cost, one per XCD; a tile's cost follows its measured duration by valid rows (below): 100 when more
+// than half of its bm rows are valid (both token halves of the block multiply), 69 or 62 otherwise (one
+// half multiplies; streaming its weights still takes most of the time). Within a range the blocks of
+// that XCD take tiles in order from a counter.
 // Exclusive prefix sum over the 512 threads of a block (buf: 512 entries of LDS, reusable on return).
 __device__ __forceinline__ long long block_exclusive_scan(long long v, long long* buf) {
   const int t = threadIdx.x;
@@ -63,7 +64,13 @@ __global__ __launch_bounds__(512) void ffn_schedule_mfma(const int32_t* __restri
   __shared__ long long s_tot[2];
   const int g = threadIdx.x;
   const bool grp = g <= E;
-  auto tile_cost = [&](int n, int m) { return min(bm, n - m * bm) > bm / 2 ? 10 : 7; };
+  // relative duration of a tile by its valid rows (measured on the V3 layer, both projections: a tile
+  // whose second half of tokens is empty skips half the MFMAs, and one of at most bm/4 rows also most
+  // of the token copies; the shared group's full tiles run a little longer than routed ones)
+  auto tile_cost = [&](int n, int m) {
+    const int r = min(bm, n - m * bm);
+    return r > bm / 2 ? (g == E ? 103 : 100) : (r > bm / 4 ? 69 : 62);
+  };
   int n = 0, mt = 0, S = 0;
   if (grp) {
     n = g < E ? offsets[g + 1] - offsets[g] : T;
