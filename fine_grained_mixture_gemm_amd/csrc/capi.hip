@@ -135,7 +135,7 @@ Layout layout(const moe_config* c) {
   L.chunk_counts = take(nch * E * 4);
   L.chunk_base = take(nch * E * 4);
   L.mt_prefix = take((E + 1) * 4);
-  L.xsched = take(2 * 9 * 4 + 2 * 8 * 4);
+  L.xsched = take(2 * (kSchedRange + kSchedCount) * 4);
   L.uq = take(fp8 ? T * d : 0);
   L.us = take(fp8 ? T * (d / 128) * 4 : 0);
   L.a_r = take(rows * f * esz_a);
@@ -207,8 +207,8 @@ BwdLayout bwd_layout(const moe_config* c) {
   L.uq = take(T * d);
   L.us = take(T * (d / 128) * 4);
   L.mt_prefix = take((E + 1) * 4);
-  L.xsched_a = take(2 * 9 * 4 + 2 * 8 * 4);
-  L.xsched_b = take(2 * 9 * 4 + 2 * 8 * 4);
+  L.xsched_a = take(2 * (kSchedRange + kSchedCount) * 4);
+  L.xsched_b = take(2 * (kSchedRange + kSchedCount) * 4);
   L.dyq_r = take(rows * d);
   L.dys_r = take(rows * (d / 128) * 4);
   L.dyq_s = take(T * d * (fs > 0));
@@ -394,7 +394,7 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   const int bm = mfma ? gemm_mfma_bm() : gemm_simt_bm();
   int32_t* mt_prefix = reinterpret_cast<int32_t*>(base + L.mt_prefix);
   int32_t* xrange = reinterpret_cast<int32_t*>(base + L.xsched);
-  int32_t* xcount = xrange + 2 * 9;
+  int32_t* xcount = xrange + 2 * kSchedRange;
   const int fs = c->n_shared * c->inter_dim;
   // a decode-sized E4M3 batch streams the touched experts' weights with its own kernels (no tile list)
   const bool decode = fp8 && c->T <= gemm_decode_max_tokens();
@@ -464,8 +464,8 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   g.out_shared = static_cast<uint8_t*>(y_s);
   g.out_scale_routed = nullptr;
   g.out_scale_shared = nullptr;
-  g.xrange = xrange + 9;
-  g.xcount = xcount + 8;
+  g.xrange = xrange + kSchedRange;
+  g.xcount = xcount + kSchedCount;
   if (decode) {
     MOE_TRY(hip_status(launch_gemm_decode(g, false, s), "down GEMM launch"));
   } else if (mfma) {
@@ -705,9 +705,9 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
   // tile ranges: (g, v) recompute [gate/up shape] and da = dy W2 [down shape, output f]; then dx [output d]
   {
     const int nt_r[2] = {f / 128, f / 256}, nt_s[2] = {fs / 128, sh ? f / 256 : 0};
-    MOE_TRY(hip_status(launch_schedule_mfma(offsets, E, T, bm, nt_r, nt_s, mt_prefix, xa, xa + 18, s), "schedule launch"));
+    MOE_TRY(hip_status(launch_schedule_mfma(offsets, E, T, bm, nt_r, nt_s, mt_prefix, xa, xa + 2 * kSchedRange, s), "schedule launch"));
     const int nt_r2[2] = {f / 128, d / 256}, nt_s2[2] = {0, sh ? d / 256 : 0};
-    MOE_TRY(hip_status(launch_schedule_mfma(offsets, E, T, bm, nt_r2, nt_s2, mt_prefix, xb, xb + 18, s), "schedule launch"));
+    MOE_TRY(hip_status(launch_schedule_mfma(offsets, E, T, bm, nt_r2, nt_s2, mt_prefix, xb, xb + 2 * kSchedRange, s), "schedule launch"));
   }
   // cached forward input: u quantized 1x128 as in the forward
   MOE_TRY(hip_status(launch_quant_act(u, true, T, d, base + L.uq, F(L.us), s), "activation quantization launch"));
@@ -722,7 +722,7 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
   g.f = f;
   g.fs = fs;
   g.xrange = xa;
-  g.xcount = xa + 18;
+  g.xcount = xa + 2 * kSchedRange;
   g.w_routed = static_cast<const uint8_t*>(layer->w13);
   g.w_shared = static_cast<const uint8_t*>(layer->ws13);
   g.ws_routed = layer->w13_scale;
@@ -738,8 +738,8 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
   g.d = f;
   g.f = d;
   g.fs = d;
-  g.xrange = xa + 9;
-  g.xcount = xa + 18 + 8;
+  g.xrange = xa + kSchedRange;
+  g.xcount = xa + 2 * kSchedRange + kSchedCount;
   g.w_routed = static_cast<const uint8_t*>(layer_t->w2);
   g.w_shared = static_cast<const uint8_t*>(layer_t->ws2);
   g.ws_routed = layer_t->w2_scale;
@@ -763,8 +763,8 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
   g.d = d;
   g.f = 2 * f;
   g.fs = 2 * fs;
-  g.xrange = xb + 9;
-  g.xcount = xb + 18 + 8;
+  g.xrange = xb + kSchedRange;
+  g.xcount = xb + 2 * kSchedRange + kSchedCount;
   g.w_routed = static_cast<const uint8_t*>(layer_t->w13);
   g.w_shared = static_cast<const uint8_t*>(layer_t->ws13);
   g.ws_routed = layer_t->w13_scale;

@@ -199,16 +199,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
   // the block has id ids[k % 4]: the ring holds the next three, and one more request is in flight.
   const int xcd = blockIdx.x & 7;
   const int t_begin = a.xrange[xcd], t_end = a.xrange[xcd + 1];
+  const int p_begin = a.xrange[8], n_tiles = a.xrange[9];
+  // the next tile id for this block: from its XCD's range, then from the shared pool; n_tiles: none left
+  auto claim = [&]() {
+    const int id = t_begin + atomicAdd(a.xcount + xcd, 1);
+    if (id < t_end) return id;
+    const int p = p_begin + atomicAdd(a.xcount + 8, 1);
+    return p < n_tiles ? p : n_tiles;
+  };
   int32_t* ids = reinterpret_cast<int32_t*>(lds + kIds);
   int pending = 0;
   if (tid == 0) {
 #pragma unroll
-    for (int k = 0; k < 3; ++k) ids[k] = t_begin + atomicAdd(a.xcount + xcd, 1);
-    pending = t_begin + atomicAdd(a.xcount + xcd, 1);
+    for (int k = 0; k < 3; ++k) ids[k] = claim();
+    pending = claim();
   }
   barrier_lds();
   int id_l = __builtin_amdgcn_readfirstlane(ids[0]);
-  if (id_l >= t_end) return;
+  if (id_l >= n_tiles) return;
   int ktile = 0;                           // tiles the loader has started, minus one
   auto next_id = [&](int k) { return __builtin_amdgcn_readfirstlane(ids[k & 3]); };
   const int nt_s = max(1, GATEUP ? a.fs / 128 : a.d / kBW);
@@ -276,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
   };
   setup();
   int id_n = next_id(1);
-  if (id_n < t_end) {
+  if (id_n < n_tiles) {
     tn = decode(id_n);
     fetch_rows(tn);
   }
@@ -287,18 +295,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
     if (kl == nst_l && live) {
       ++ktile;
       id_l = next_id(ktile);
-      if (id_l < t_end) {
+      if (id_l < n_tiles) {
         setup();
         ++started;
         id_n = next_id(ktile + 1);
-        if (id_n < t_end) {
+        if (id_n < n_tiles) {
           tn = decode(id_n);
           fetch_rows(tn);
         }
         // the id of tile ktile + 2 arrived a tile ago; request the one after it
         if (tid == 0) {
           ids[(ktile + 2) & 3] = pending;
-          pending = t_begin + atomicAdd(a.xcount + xcd, 1);
+          pending = claim();
         }
       } else {
         live = false;

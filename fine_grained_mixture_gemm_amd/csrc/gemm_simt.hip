@@ -33,10 +33,11 @@ hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_pr
 
 // Schedule of the matrix-core grouped GEMMs. The tile list (routed experts ascending, M index fastest
 // within an N tile, then the shared group) is cut into eight contiguous ranges of equal estimated
-// cost, one per XCD; a tile's cost follows its measured duration by valid rows (below): 100 when more
+// cost, one per XCD, over the first 7/8 of the total; the rest is a pool for any XCD whose range is
+// done. A tile's cost follows its measured duration by valid rows (below): 100 when more
 // than half of its bm rows are valid (both token halves of the block multiply), 69 or 62 otherwise (one
 // half multiplies; streaming its weights still takes most of the time). Within a range the blocks of
-// that XCD take tiles in order from a counter.
+// that XCD take tiles in order from a counter, then from the pool's.
 // Exclusive prefix sum over the 512 threads of a block (buf: 512 entries of LDS, reusable on return).
 __device__ __forceinline__ long long block_exclusive_scan(long long v, long long* buf) {
   const int t = threadIdx.x;
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(512) void ffn_schedule_mfma(const int32_t* __restri
     mt = cdiv(n, bm);
     for (int m = 0; m < mt; ++m) S += tile_cost(n, m);
   }
-  if (g < 16) xcount[g] = 0;
+  if (g < 2 * kSchedCount) xcount[g] = 0;
   // M tiles before each routed group; for g = E this is their total
   const long long mpre = block_exclusive_scan(g < E ? mt : 0, buf);
   if (grp) mt_prefix[g] = (int)mpre;
@@ -93,16 +94,19 @@ __global__ __launch_bounds__(512) void ffn_schedule_mfma(const int32_t* __restri
     }
     __syncthreads();
     const long long total = s_tot[0];
-    int32_t* r = xrange + 9 * l;
+    const long long ranged = total - total / kSchedPoolDiv;   // cost of the XCD ranges; the rest is the pool
+    int32_t* r = xrange + kSchedRange * l;
     if (g == 0) {
       r[0] = 0;
-      r[8] = (int)s_tot[1];
+      r[9] = (int)s_tot[1];
+      if (ranged <= 0) r[8] = 0;
     }
-    // boundary x: the first tile whose preceding cost reaches x * total / 8. The groups with tiles split
-    // (0, total] into the intervals (before, before + C]; the owner's tiles are nt equal columns of cost S
-    // (M fastest within an N column): it skips whole columns, then scans the M tiles of the next one.
-    for (int x = 1; x < 8; ++x) {
-      const long long tgt = total * x / 8;
+    // boundary x: the first tile whose preceding cost reaches x * ranged / 8 (x = 8: the pool's start).
+    // The groups with tiles split (0, total] into the intervals (before, before + C]; the owner's tiles are
+    // nt equal columns of cost S (M fastest within an N column): it skips whole columns, then scans the M
+    // tiles of the next one.
+    for (int x = 1; x <= 8; ++x) {
+      const long long tgt = ranged * x / 8;
       if (tgt <= 0) {
         if (g == 0) r[x] = 0;
         continue;

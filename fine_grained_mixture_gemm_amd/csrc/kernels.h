@@ -90,8 +90,8 @@ struct GemmArgs {
   const int32_t* offsets;
   const int32_t* perm_src;
   const int32_t* mt_prefix;   // [E+1] prefix of M tiles per routed expert
-  const int32_t* xrange;      // matrix-core path: [9] tile-id range of each XCD (cost-balanced)
-  int32_t* xcount;            // matrix-core path: [8] per-XCD tile counters, zero at launch
+  const int32_t* xrange;      // matrix-core path: [kSchedRange] tile-id ranges (see launch_schedule_mfma)
+  int32_t* xcount;            // matrix-core path: [kSchedCount] tile counters, zero at launch
   const uint8_t* w_routed;    // w13 or w2 of all routed experts
   const uint8_t* w_shared;
   const float* ws_routed;     // fp8 block scales
@@ -115,7 +115,11 @@ hipError_t launch_quant_act(const void* x, bool x_bf16, int rows, int cols, uint
 hipError_t launch_quant_weight(const float* w, int batch, int rows, int cols, uint8_t* q, float* scales, hipStream_t s);
 hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_prefix, hipStream_t s);
 // M-tile prefix plus, for the gate/up (k = 0) and down (k = 1) launches of the matrix-core GEMM, the
-// cost-balanced XCD ranges xrange[k][9] and zeroed tile counters xcount[k][8].
+// tile ranges xrange[k][kSchedRange] and zeroed tile counters xcount[k][kSchedCount]: tiles
+// [xrange[x], xrange[x + 1]) belong to XCD x (x < 8, equal estimated cost), [xrange[8], xrange[9]) are a
+// pool that any block takes from once its XCD's range is done (counter 8; the last 1/kSchedPoolDiv of
+// the cost), so that blocks of every XCD finish together.
+constexpr int kSchedRange = 10, kSchedCount = 9, kSchedPoolDiv = 8;
 hipError_t launch_schedule_mfma(const int32_t* offsets, int E, int T, int bm, const int (&nt_r)[2], const int (&nt_s)[2],
                                 int32_t* mt_prefix, int32_t* xrange, int32_t* xcount, hipStream_t s);
 int gemm_mfma_bm();
