@@ -136,7 +136,7 @@ constexpr int wgrad_q_lds() {
 
 // pblk[g] = first row block of group g (routed experts 0..E-1, then the shared block, empty unless
 // `shared`), pblk[E + 1] = their total: ceil(n_g / 128) blocks per group. One block, a scan over LDS.
-// pblk[E + 2 .. E + 17] are cleared: the tile counters of the two weight-gradient GEMMs.
+// pblk[E + 2 .. E + 19] are cleared: the tile counters of the two weight-gradient GEMMs.
 __global__ __launch_bounds__(512) void wgrad_block_prefix(const int32_t* __restrict__ offsets, int E, int T,
                                                           int shared, int32_t* __restrict__ pblk) {
   __shared__ int buf[512];
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(512) void wgrad_block_prefix(const int32_t* __restr
   }
   if (g <= E) pblk[g + 1] = buf[g];
   if (g == 0) pblk[0] = 0;
-  if (g < 16) pblk[E + 2 + g] = 0;   // the weight-gradient GEMMs' tile counters
+  if (g < 18) pblk[E + 2 + g] = 0;   // the weight-gradient GEMMs' tile counters (9 per launch)
 }
 
 // The group holding row block b: the last g with pblk[g] <= b (a non-empty group; b < pblk[E + 1]).
@@ -331,9 +331,10 @@ __global__ __launch_bounds__(256) void wgrad_quant_rows(WgQuantArgs a) {
 // column order that gives each lane 8 adjacent columns of one output row per pair of 16-column MFMA
 // tiles, and a tile's bf16 result is stored during the next tile's first stage (its stores then complete
 // behind that stage's MFMAs). Tile list: the shared block first (the longest contraction), then the
-// routed experts; inside a group the output rows run fastest. The list is cut into eight ranges of equal
-// estimated cost (stages + 1 per tile), one per XCD (block id mod 8), whose blocks take tiles in order
-// from the XCD's counter. A tile of an empty group multiplies nothing and stores zeros.
+// routed experts; inside a group the output rows run fastest. The first 7/8 of the list's estimated cost
+// (stages + 1 per tile) is cut into eight ranges, one per XCD (block id mod 8), whose blocks take tiles in
+// order from the XCD's counter and then from the pool of the remaining tiles. A tile of an empty group
+// multiplies nothing and stores zeros.
 constexpr int kWgT = 256;
 constexpr int kWgThreads = 512;
 constexpr int kWgOp = kWgT * 128;                  // one operand of a stage: 256 rows x 128 bytes
@@ -366,9 +367,11 @@ __global__ __launch_bounds__(kWgThreads, 1) void grouped_wgrad_mfma(WgGemmArgs a
   auto group_at = [&](int go) { return has_shared ? (go == 0 ? E : go - 1) : go; };
   // first tile of XCD x's range: cost of the tiles before tile go * tpg + r is tpg (stages_before(go) + go)
   // + r (stages of group go + 1)
+  // the eight XCD ranges cover the first 7/8 of the cost; the tiles after them are a pool (counter 8)
   auto range_start = [&](int x) {
-    if (x >= 8) return G * tpg;
-    const long long target = (long long)tpg * (S + G) * x / 8;
+    if (x >= 9) return G * tpg;
+    const long long ranged = (long long)tpg * (S + G) - (long long)tpg * (S + G) / 8;
+    const long long target = ranged * x / 8;
     int lo = 0, hi = G;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -381,16 +384,24 @@ __global__ __launch_bounds__(kWgThreads, 1) void grouped_wgrad_mfma(WgGemmArgs a
   };
   const int xcd = blockIdx.x & 7;
   const int t_begin = range_start(xcd), t_end = range_start(xcd + 1);
+  const int p_begin = range_start(8), n_tiles = G * tpg;
+  // the next tile id: from this XCD's range, then from the pool; n_tiles: none left
+  auto claim = [&]() {
+    const int id = t_begin + atomicAdd(a.xcount + xcd, 1);
+    if (id < t_end) return id;
+    const int p = p_begin + atomicAdd(a.xcount + 8, 1);
+    return p < n_tiles ? p : n_tiles;
+  };
   int32_t* ids = reinterpret_cast<int32_t*>(lds + kWgIds);
   int pending = 0;
   if (tid == 0) {
 #pragma unroll
-    for (int k = 0; k < 3; ++k) ids[k] = t_begin + atomicAdd(a.xcount + xcd, 1);
-    pending = t_begin + atomicAdd(a.xcount + xcd, 1);
+    for (int k = 0; k < 3; ++k) ids[k] = claim();
+    pending = claim();
   }
   barrier_lds();
   int id_l = __builtin_amdgcn_readfirstlane(ids[0]);
-  if (id_l >= t_end) return;
+  if (id_l >= n_tiles) return;
   int ktile = 0;
 
   // ---- loader. Thread tid moves, per stage and operand, the 16-byte pieces 512 q + tid (q < 4): LDS row
@@ -445,14 +456,14 @@ __global__ __launch_bounds__(kWgThreads, 1) void grouped_wgrad_mfma(WgGemmArgs a
     if (kl == nst_l && live) {
       ++ktile;
       id_l = __builtin_amdgcn_readfirstlane(ids[ktile & 3]);
-      if (id_l < t_end) {
+      if (id_l < n_tiles) {
         tl = decode(id_l);
         setup();
         ++started;
         // the id of tile ktile + 2 arrived a tile ago; request the one after it
         if (tid == 0) {
           ids[(ktile + 2) & 3] = pending;
-          pending = t_begin + atomicAdd(a.xcount + xcd, 1);
+          pending = claim();
         }
       } else {
         live = false;

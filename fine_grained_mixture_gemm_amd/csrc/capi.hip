@@ -224,7 +224,7 @@ BwdLayout bwd_layout(const moe_config* c) {
   L.nblk = wgrad_row_blocks_max(c->T, c->top_k, c->n_routed, fs > 0);
   L.rpad = (size_t)L.nblk * 128;
   const size_t nb = L.nblk;
-  L.pblk = take((E + 2 + 16) * 4);
+  L.pblk = take((E + 2 + 18) * 4);
   L.wq_dy = take(d * L.rpad);
   L.ws_dy = take(nb * d * 4);
   L.wq_a = take(f * L.rpad);
@@ -306,7 +306,7 @@ moe_status weight_gradients(const moe_config* c, const BwdLayout& L, uint8_t* ba
   g.Bs = F(L.ws_dgv);
   g.out_r = static_cast<uint16_t*>(dw13);
   g.out_s = static_cast<uint16_t*>(dws13);
-  g.xcount = pblk + E + 10;
+  g.xcount = pblk + E + 11;
   MOE_TRY(hip_status(launch_wgrad_gemm(g, grid, s), "dW13 GEMM launch"));
   return MOE_OK;
 }

@@ -149,7 +149,7 @@ struct WgQuantArgs {
 };
 struct WgGemmArgs {
   const int32_t* pblk;
-  int32_t* xcount;            // 8 tile counters (one per XCD), zero at launch
+  int32_t* xcount;            // 9 tile counters (one per XCD, then the pool's), zero at launch
   int E, shared, M, N;        // output [M][N] per group (multiples of 128)
   const uint8_t* A;           // [N][rpad] codes, scales As [row block][N]
   const float* As;
@@ -160,7 +160,7 @@ struct WgGemmArgs {
   uint16_t* out_s;            // bf16 [M][N]
 };
 int wgrad_row_blocks_max(int T, int K, int E, bool shared);
-// pblk[0..E+1], then 16 zeroed tile counters (two launches of the weight-gradient GEMM)
+// pblk[0..E+1], then 18 zeroed tile counters (two launches of the weight-gradient GEMM)
 hipError_t launch_wgrad_prefix(const int32_t* offsets, int E, int T, bool shared, int32_t* pblk, hipStream_t s);
 hipError_t launch_wgrad_quant(const WgQuantArgs& a, int src, int nblk_max, hipStream_t s);
 hipError_t launch_wgrad_gemm(const WgGemmArgs& a, int grid, hipStream_t s);   // grid >= 8 (one block per CU)
