@@ -1,6 +1,7 @@
 // Combine (DeepSeek Technical Report: MoE Architecture, 1.1 and 5.3 [1]):
 //   h_t = u_t + y_shared_t + sum_k g_{t,k} * y[row_of(t,k)]
 // summed in fp32 in that order (k ascending = expert ascending), rounded once to the output dtype.
+// A pair that dispatch dropped (row_of = -1: no routed expert, or a repeated one) adds nothing.
 // One 256-thread block per token; each thread reads and writes 16-byte pieces of the rows, so every
 // row access is a contiguous, coalesced sweep.
 //
@@ -63,10 +64,12 @@ __global__ __launch_bounds__(256) void combine_rows(const void* __restrict__ u_,
       uint4 raw[kCombineMaxK];
 #pragma unroll
       for (int k = 0; k < kCombineMaxK; ++k)
-        if (k < K) raw[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(yr_) + (size_t)s_row[k] * d + col);
+        if (k < K && s_row[k] >= 0)
+          raw[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(yr_) + (size_t)s_row[k] * d + col);
 #pragma unroll
       for (int k = 0; k < kCombineMaxK; ++k) {
         if (k >= K) break;
+        if (s_row[k] < 0) continue;
         const float g = s_g[k];
         const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
 #pragma unroll
@@ -77,6 +80,7 @@ __global__ __launch_bounds__(256) void combine_rows(const void* __restrict__ u_,
       }
     } else {
       for (int k = 0; k < K; ++k) {
+        if (s_row[k] < 0) continue;
         load8(yr_, YBF16, (size_t)s_row[k] * d + col, y);
         const float g = s_g[k];
 #pragma unroll
@@ -100,7 +104,8 @@ __global__ __launch_bounds__(256) void combine_rows(const void* __restrict__ u_,
   for (int c = nvec * 8 + threadIdx.x; c < d; c += blockDim.x) {
     float acc = load1(u_, BF16, (size_t)t * d + c);
     if (ys_) acc += load1(ys_, YBF16, (size_t)t * d + c);
-    for (int k = 0; k < K; ++k) acc = fmaf(s_g[k], load1(yr_, YBF16, (size_t)s_row[k] * d + c), acc);
+    for (int k = 0; k < K; ++k)
+      if (s_row[k] >= 0) acc = fmaf(s_g[k], load1(yr_, YBF16, (size_t)s_row[k] * d + c), acc);
     if constexpr (BF16) static_cast<uint16_t*>(h_)[(size_t)t * d + c] = f32_to_bf16(acc);
     else static_cast<float*>(h_)[(size_t)t * d + c] = acc;
   }

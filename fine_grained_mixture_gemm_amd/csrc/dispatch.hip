@@ -13,6 +13,16 @@ namespace moe {
 constexpr int kChunk = 256;
 constexpr int kWords = kChunk / 32;
 
+// A (token, slot) pair enters the permutation when its id names a routed expert and no earlier slot of
+// the token holds the same id: one row per (token, expert). Other pairs are dropped (row_of = -1).
+__device__ __forceinline__ bool pair_kept(const int32_t* __restrict__ ids, int k, int E) {
+  const int e = ids[k];
+  if (e < 0 || e >= E) return false;
+  for (int j = 0; j < k; ++j)
+    if (ids[j] == e) return false;
+  return true;
+}
+
 __device__ __forceinline__ void build_bits(uint32_t (*bits)[kWords], const int32_t* __restrict__ idx, int T, int E,
                                            int K, int c) {
   for (int i = threadIdx.x; i < E * kWords; i += blockDim.x) (&bits[0][0])[i] = 0u;
@@ -21,7 +31,7 @@ __device__ __forceinline__ void build_bits(uint32_t (*bits)[kWords], const int32
   if (t < T) {
     for (int k = 0; k < K; ++k) {
       const int e = idx[(size_t)t * K + k];
-      if (e >= 0 && e < E) atomicOr(&bits[e][tl >> 5], 1u << (tl & 31));
+      if (pair_kept(idx + (size_t)t * K, k, E)) atomicOr(&bits[e][tl >> 5], 1u << (tl & 31));
     }
   }
   __syncthreads();
@@ -79,7 +89,10 @@ __global__ __launch_bounds__(kChunk) void dispatch_scatter(const int32_t* __rest
   const uint32_t below = (1u << (tl & 31)) - 1u;
   for (int k = 0; k < K; ++k) {
     const int e = idx[(size_t)t * K + k];
-    if (e < 0 || e >= E) continue;   // not an expert id: the pair is dropped
+    if (!pair_kept(idx + (size_t)t * K, k, E)) {
+      row_of[(size_t)t * K + k] = -1;
+      continue;
+    }
     int rank = __popc(bits[e][w0] & below);
     for (int w = 0; w < w0; ++w) rank += __popc(bits[e][w]);
     const int row = offsets[e] + chunk_base[(size_t)c * E + e] + rank;

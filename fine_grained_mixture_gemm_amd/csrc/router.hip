@@ -258,7 +258,8 @@ __device__ __forceinline__ float wave_topk_f32(const float key[4], const bool va
     if (r == K - 1) kth = kv;
     if (r == K) k1 = kv;
   }
-  return kth - k1;
+  // no (K+1)-th key when K == E: the selection is decided by construction
+  return rounds > K ? kth - k1 : __builtin_inff();
 }
 
 // Group-limited routing on one wave (DeepSeek Technical Report: MoE Architecture, 2.3 device-limited

@@ -121,12 +121,20 @@ moe_status moe_route(const moe_config* cfg, const moe_layer* layer, const void* 
 moe_status moe_router_logits(const moe_config* cfg, const moe_layer* layer, const void* u, float* z, void* ws,
                              size_t ws_bytes, hipStream_t stream);
 
-/* Dispatch: expert histogram, exclusive prefix sum and permutation into expert-contiguous rows.
- *  topk_idx [T, K] int32 in (as written by moe_route: distinct experts per token).
- *  counts   [E] int32 out: tokens per routed expert (sums to T*K).
+/* Dispatch (DeepSeek Technical Report: MoE Architecture, 1.1: the routed sum of the layer runs over the
+ * K experts of TopK(t) only, so each token's row goes to its K experts; 3.6 names this step, the
+ * all-to-all dispatch of the multi-GPU design, whose payload is the E4M3 activation. On one GPU it is a
+ * permutation: expert histogram, exclusive prefix sum and a stable order of the (token, slot) pairs by
+ * expert. The 1x128 E4M3 quantization of u is not done here but by moe_expert_ffn, which gathers the
+ * quantized rows of u through perm_src instead of reading a permuted copy).
+ *  topk_idx [T, K] int32 in (as written by moe_route: distinct experts per token). A pair whose id is
+ *           outside [0, E) or repeats an id of an earlier slot of the same token is dropped: it gets no
+ *           row, is not counted, and its row_of entry is -1 (moe_combine adds nothing for it).
+ *  counts   [E] int32 out: tokens per routed expert (sums to T*K when no pair is dropped).
  *  offsets  [E+1] int32 out: exclusive prefix sum of counts; rows of expert e are offsets[e]..offsets[e+1]-1.
- *  perm_src [T*K] int32 out: token of each row; tokens ascend within an expert.
- *  row_of   [T, K] int32 out: row of each (token, slot) pair, so perm_src[row_of[t][k]] == t. */
+ *  perm_src [T*K] int32 out: token of each row; tokens ascend within an expert. Entries past
+ *           offsets[E] are not written.
+ *  row_of   [T, K] int32 out: row of each (token, slot) pair, so perm_src[row_of[t][k]] == t, or -1. */
 moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
                         int32_t* perm_src, int32_t* row_of, void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -142,14 +150,21 @@ moe_status moe_expert_ffn(const moe_config* cfg, const moe_layer* layer, const v
                           const int32_t* perm_src, void* y_routed, void* y_shared, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
-/* Combine: h_t = u_t + y_shared_t + sum_k topk_w[t][k] * y_routed[row_of[t][k]], summed in fp32 in
- * that order (k ascending = expert ascending) and rounded once to act_dtype.
+/* Combine (DeepSeek Technical Report: MoE Architecture, 1.1 and 5.3 [1]: the layer output is the input
+ * plus the shared experts' outputs plus the gate-weighted outputs of the selected routed experts; 3.6
+ * sends the routed outputs back in BF16, the dtype of y_routed for E4M3 experts):
+ *   h_t = u_t + y_shared_t + sum_k topk_w[t][k] * y_routed[row_of[t][k]],
+ * summed in fp32 in that order (k ascending = expert ascending) and rounded once to act_dtype. A pair
+ * with row_of[t][k] = -1 (dropped by moe_dispatch) adds nothing; any other entry must be a row below T*K.
  *  y_shared may be NULL when Ks == 0.  h [T, d] act_dtype out (must not alias the inputs). */
 moe_status moe_combine(const moe_config* cfg, const void* u, const void* y_routed, const void* y_shared,
                        const int32_t* row_of, const float* topk_w, void* h, hipStream_t stream);
 
-/* The whole layer: moe_route, moe_dispatch, moe_expert_ffn and moe_combine on `stream`, with every
- * intermediate in the workspace. topk_idx [T, K] and counts [E] are optional outputs (NULL to skip). */
+/* The whole layer (DeepSeek Technical Report: MoE Architecture, 1.1 "Shared Expert Isolation" formula
+ * and 5.3 [1]; gating as in moe_route, experts as in moe_expert_ffn): moe_route, moe_dispatch,
+ * moe_expert_ffn and moe_combine on `stream`, with every intermediate in the workspace. topk_idx [T, K]
+ * and counts [E] are optional outputs (NULL to skip). The bias is read, never written: the update of
+ * auxiliary-loss-free balancing is the separate call moe_update_bias, made after the step. */
 moe_status moe_forward(const moe_config* cfg, const moe_layer* layer, const void* u, const float* bias, void* h,
                        int32_t* topk_idx, int32_t* counts, void* ws, size_t ws_bytes, hipStream_t stream);
 
