@@ -17,7 +17,7 @@ __all__ = [
     "moe_expert_ffn", "moe_combine", "moe_forward", "moe_update_bias", "moe_quantize_weights",
     "moe_quantize_act", "moe_last_error", "moe_set_timing_events", "MOE_NUM_MARKS", "MARK_NAMES", "LIB_PATH",
     "moe_balance_stats", "moe_backward_workspace_size", "moe_expert_ffn_backward_input", "moe_transpose_fp8_weights",
-    "moe_expert_ffn_backward",
+    "moe_expert_ffn_backward", "moe_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES",
 ]
 
 # MOE_LIBRARY_PATH overrides the in-tree library (a developer switch for comparing builds).
@@ -61,6 +61,7 @@ _SIGS = {
     "moe_expert_ffn": [_CP, _LP, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_combine": [_CP, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_forward": [_CP, _LP, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "moe_forward_noalloc": [_CP, _LP, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_update_bias": [_CP, _vp, _f32, _vp, _vp],
     "moe_balance_stats": [_CP, _vp, _vp, _i32, _f32, _f32, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_backward_workspace_size": [_CP, ctypes.POINTER(_sz)],
@@ -153,6 +154,14 @@ def moe_combine(cfg, u, y_routed, y_shared, row_of, topk_w, h, stream=None):
 def moe_forward(cfg, layer, u, bias, h, topk_idx, counts, ws, stream=None):
     _call("moe_forward", ctypes.byref(cfg), ctypes.byref(layer), _dev(u), _dev(bias), _dev(h), _dev(topk_idx),
           _dev(counts), _dev(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_noalloc(cfg, layer, u, bias, h, topk_idx, counts, stream=None):
+    _call("moe_forward_noalloc", ctypes.byref(cfg), ctypes.byref(layer), _dev(u), _dev(bias), _dev(h), _dev(topk_idx),
+          _dev(counts), _stream(stream))
 
 
 def moe_update_bias(cfg, counts, gamma, bias, stream=None):

@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -539,8 +540,8 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, int32_t*
   Layout L;
   MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
   if (cfg->T == 0) {
-    MOE_TRY(hip_status(hipMemsetAsync(counts, 0, sizeof(int32_t) * cfg->n_routed, stream), "memset counts"));
-    return hip_status(hipMemsetAsync(offsets, 0, sizeof(int32_t) * (cfg->n_routed + 1), stream), "memset offsets");
+    MOE_TRY(hip_status(launch_zero_fill(counts, sizeof(int32_t) * cfg->n_routed, stream), "counts clear"));
+    return hip_status(launch_zero_fill(offsets, sizeof(int32_t) * (cfg->n_routed + 1), stream), "offsets clear");
   }
   return do_dispatch(cfg, topk_idx, counts, offsets, perm_src, row_of, base, L, stream);
 }
@@ -584,7 +585,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_layer* layer, const void
   int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(base + L.f_idx);
   int32_t* cnt = counts ? counts : reinterpret_cast<int32_t*>(base + L.f_counts);
   if (cfg->T == 0) {
-    if (counts) return hip_status(hipMemsetAsync(counts, 0, sizeof(int32_t) * cfg->n_routed, stream), "memset counts");
+    if (counts) return hip_status(launch_zero_fill(counts, sizeof(int32_t) * cfg->n_routed, stream), "counts clear");
     return MOE_OK;
   }
   float* w = reinterpret_cast<float*>(base + L.f_w);
@@ -601,6 +602,48 @@ moe_status moe_forward(const moe_config* cfg, const moe_layer* layer, const void
                      "combine launch"));
   mark(MOE_MARK_COMBINE_END, stream);
   return MOE_OK;
+}
+
+// ------------------------------------------------------------------ allocation-free forward
+// Scratch of moe_forward_noalloc: one copy per GPU, held from the library's load on that GPU until the
+// process ends. Host code never passes `scratch` itself to a kernel or a copy: it is a host-side stand-in;
+// the device address of a GPU's copy comes from hipGetSymbolAddress with that GPU current.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current GPU's scratch, looked up once per GPU.
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  MOE_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    MOE_TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_forward_noalloc(const moe_config* cfg, const moe_layer* layer, const void* u, const float* bias, void* h,
+                               int32_t* topk_idx, int32_t* counts, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const size_t need = layout(cfg).total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_forward_noalloc: this configuration needs %zu bytes of scratch, above the library's static %zu "
+                "(use moe_forward with a workspace)",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  MOE_TRY(scratch_of_current_device(&ws));
+  return moe_forward(cfg, layer, u, bias, h, topk_idx, counts, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float gamma, float* bias, hipStream_t stream) {
@@ -683,12 +726,12 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
     // no rows: every weight gradient is zero
     if (want_dw) {
       const size_t n13 = (size_t)c->n_routed * 2 * c->inter_dim * c->d_model * 2, n2 = n13 / 2;
-      MOE_TRY(hip_status(hipMemsetAsync(dw13, 0, n13, stream), "weight gradient clear"));
-      MOE_TRY(hip_status(hipMemsetAsync(dw2, 0, n2, stream), "weight gradient clear"));
+      MOE_TRY(hip_status(launch_zero_fill(dw13, n13, stream), "weight gradient clear"));
+      MOE_TRY(hip_status(launch_zero_fill(dw2, n2, stream), "weight gradient clear"));
       if (sh) {
         const size_t s13 = (size_t)2 * c->inter_dim * c->d_model * 2;
-        MOE_TRY(hip_status(hipMemsetAsync(dws13, 0, s13, stream), "weight gradient clear"));
-        MOE_TRY(hip_status(hipMemsetAsync(dws2, 0, s13 / 2, stream), "weight gradient clear"));
+        MOE_TRY(hip_status(launch_zero_fill(dws13, s13, stream), "weight gradient clear"));
+        MOE_TRY(hip_status(launch_zero_fill(dws2, s13 / 2, stream), "weight gradient clear"));
       }
     }
     return MOE_OK;

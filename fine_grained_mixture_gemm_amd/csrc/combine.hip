@@ -7,6 +7,8 @@
 //
 // Bias update (same report, 3.3): b_i - gamma for an overloaded expert, b_i + gamma for an
 // underloaded one, unchanged at the mean load; decided in integers as counts_i * E against T * K.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -129,6 +131,27 @@ __global__ void bias_update_kernel(const int32_t* __restrict__ counts, int E, lo
   const float b = bias[e];
   if (load > TK) bias[e] = b - gamma;
   else if (load < TK) bias[e] = b + gamma;
+}
+
+// Zero `bytes` bytes at p (a small fill kernel instead of a memset node, so that a captured graph replays it
+// like any other kernel).
+__global__ __launch_bounds__(256) void zero_fill(uint8_t* __restrict__ p, size_t bytes) {
+  const size_t n16 = bytes / 16, stride = (size_t)gridDim.x * blockDim.x;
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool aligned = (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+  if (aligned) {
+    for (size_t i = t; i < n16; i += stride) reinterpret_cast<uint4*>(p)[i] = make_uint4(0, 0, 0, 0);
+    for (size_t i = n16 * 16 + t; i < bytes; i += stride) p[i] = 0;
+  } else {
+    for (size_t i = t; i < bytes; i += stride) p[i] = 0;
+  }
+}
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((bytes / 16 + 255) / 256 + 1, 4096);
+  zero_fill<<<(unsigned)blocks, 256, 0, s>>>(static_cast<uint8_t*>(p), bytes);
+  return hipGetLastError();
 }
 
 hipError_t launch_bias_update(const int32_t* counts, int E, long long TK, float gamma, float* bias, hipStream_t s) {

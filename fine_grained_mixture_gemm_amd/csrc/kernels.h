@@ -174,6 +174,7 @@ int gemm_simt_bm();
 hipError_t launch_gemm_simt(const GemmArgs& a, bool gateup, int max_tiles, hipStream_t s);
 hipError_t launch_combine(const void* u, bool bf16, const void* y_routed, const void* y_shared, bool y_bf16,
                           const int32_t* row_of, const float* topk_w, int T, int d, int K, void* h, hipStream_t s);
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_bias_update(const int32_t* counts, int E, long long TK, float gamma, float* bias, hipStream_t s);
 
 }  // namespace moe

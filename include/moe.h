@@ -168,6 +168,22 @@ moe_status moe_combine(const moe_config* cfg, const void* u, const void* y_route
 moe_status moe_forward(const moe_config* cfg, const moe_layer* layer, const void* u, const float* bias, void* h,
                        int32_t* topk_idx, int32_t* counts, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the static scratch that moe_forward_noalloc uses on each GPU (64 MiB: the V3-shaped layer up to
+ * 256 tokens, a 2048-wide 64-expert layer up to 256 tokens). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_forward without a caller workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments, results and
+ * errors as moe_forward; the intermediates live in a static array of MOE_NOALLOC_SCRATCH_BYTES bytes that
+ * the library holds on every GPU it runs on until the process ends. The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); the first call on a GPU looks up the address of that
+ * GPU's array. A configuration whose moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES returns
+ * MOE_ERR_WORKSPACE before anything is launched. Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (other streams, other threads) race: serialize them. Nothing in the array
+ * needs to start at any value; each call writes every intermediate before reading it. */
+moe_status moe_forward_noalloc(const moe_config* cfg, const moe_layer* layer, const void* u, const float* bias, void* h,
+                               int32_t* topk_idx, int32_t* counts, hipStream_t stream);
+
 /* Bias update of auxiliary-loss-free balancing (DeepSeek Technical Report: MoE Architecture, 3.3):
  * b_i <- b_i - gamma if expert i is overloaded, b_i + gamma if underloaded, where overloaded means
  * counts[i] * E > T * K (load above the mean), underloaded the reverse; b_i is unchanged at the mean.

@@ -174,3 +174,14 @@ def test_full_backward_argument_errors():
     assert call(dxs=None, dw13=None) == moe.MOE_ERR_INVALID_ARG       # shared dx missing
     assert call(nbytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert "dw" in moe.moe_last_error() or "workspace" in moe.moe_last_error()
+
+
+def test_noalloc_forward_rejects_oversized_configs_before_any_launch():
+    # the V3-shaped layer at 8192 tokens needs about 1.3 GB of scratch, far above the static array
+    cfg = _cfg(T=8192, d_model=7168, n_routed=256, top_k=8, inter_dim=2048)
+    assert moe.moe_workspace_size(cfg) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    lay = moe.moe_layer()
+    st = lib.moe_forward_noalloc(ctypes.byref(cfg), ctypes.byref(lay), None, None, None, None, None, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    assert "scratch" in moe.moe_last_error()
