@@ -17,11 +17,11 @@ __all__ = [
     "moe_expert_ffn", "moe_combine", "moe_forward", "moe_update_bias", "moe_quantize_weights",
     "moe_quantize_act", "moe_last_error", "moe_set_timing_events", "MOE_NUM_MARKS", "MARK_NAMES", "LIB_PATH",
     "moe_balance_stats", "moe_backward_workspace_size", "moe_expert_ffn_backward_input", "moe_transpose_fp8_weights",
-    "moe_expert_ffn_backward", "moe_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES",
+    "moe_expert_ffn_backward", "moe_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES", "moe_route_margin",
 ]
 
-# MOE_LIBRARY_PATH overrides the in-tree library (a developer switch for comparing builds).
-LIB_PATH = os.environ.get("MOE_LIBRARY_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# always the in-tree build, next to this file
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python fine_grained_mixture_gemm_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
@@ -55,6 +55,7 @@ _vp, _sz, _i32, _f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.
 _CP, _LP = ctypes.POINTER(moe_config), ctypes.POINTER(moe_layer)
 _SIGS = {
     "moe_workspace_size": [_CP, ctypes.POINTER(_sz)],
+    "moe_route_margin": [_CP, ctypes.POINTER(_f32)],
     "moe_route": [_CP, _LP, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_router_logits": [_CP, _LP, _vp, _vp, _vp, _sz, _vp],
     "moe_dispatch": [_CP, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -123,6 +124,12 @@ def moe_workspace_size(cfg) -> int:
     n = _sz(0)
     _call("moe_workspace_size", ctypes.byref(cfg), ctypes.byref(n))
     return n.value
+
+
+def moe_route_margin(cfg) -> float:
+    d = _f32(0)
+    _call("moe_route_margin", ctypes.byref(cfg), ctypes.byref(d))
+    return d.value
 
 
 def moe_route(cfg, layer, u, bias, topk_idx, topk_w, ws, stream=None):

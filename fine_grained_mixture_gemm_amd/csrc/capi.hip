@@ -42,9 +42,11 @@ moe_status hip_status(hipError_t e, const char* what) {
     if (_s != MOE_OK) return _s;        \
   } while (0)
 
-// Tokens whose K-th and (K+1)-th fp32 keys differ by less than this are decided from fp64 logits. The
-// margins are at least 20x the largest fp32 key error measured against fp64 logits on the synthetic
-// layers: 1.7e-6 for sigmoid keys at d = 7168, 6.4e-6 for softmax keys (logits) at d = 1024.
+// Tokens whose K-th and (K+1)-th fp32 keys differ by less than this (times max(1, |u_t| max_i |e_i| /
+// sqrt(d)), the size of the token's partial sums against token rows of RMS 1 and centroids of norm 1) are
+// decided from fp64 logits. The base margins are at least 20x the largest fp32 key error measured
+// against fp64 logits on the synthetic layers: 1.7e-6 for sigmoid keys at d = 7168, 6.4e-6 for softmax
+// keys (logits) at d = 1024.
 constexpr float kRecheckDeltaSigmoid = 4e-5f;
 constexpr float kRecheckDeltaSoftmax = 2e-4f;
 
@@ -103,7 +105,7 @@ moe_status check_cfg(const moe_config* c) {
 }
 
 struct Layout {
-  size_t z, z64, wg_split, zpart, recheck_count, recheck_list;
+  size_t z, z64, wg_split, zpart, recheck_count, recheck_list, wn2;
   size_t chunk_counts, chunk_base, mt_prefix, xsched;
   size_t uq, us, a_r, a_s, as_r, as_s;
   size_t f_idx, f_w, f_counts, f_offsets, f_perm, f_rowof, f_yr, f_ys;
@@ -132,6 +134,7 @@ Layout layout(const moe_config* c) {
   L.zpart = take(ksplit > 1 ? (size_t)ksplit * T * E * 8 : 0);
   L.recheck_count = take(16);
   L.recheck_list = take(T * 4);
+  L.wn2 = take(E * 4);
   const size_t nch = dispatch_chunks(c->T);
   L.chunk_counts = take(nch * E * 4);
   L.chunk_base = take(nch * E * 4);
@@ -348,6 +351,7 @@ RouteArgs route_args(const moe_config* c, const moe_layer* l, const void* u, con
   a.n_groups = c->n_groups;
   a.topk_groups = c->topk_groups;
   a.delta = c->gate == MOE_GATE_SOFTMAX ? kRecheckDeltaSoftmax : kRecheckDeltaSigmoid;
+  a.wn2 = reinterpret_cast<float*>(base + L.wn2);
   a.z = reinterpret_cast<float*>(base + L.z);
   a.z64 = reinterpret_cast<double*>(base + L.z64);
   a.wg_split = reinterpret_cast<uint16_t*>(base + L.wg_split);
@@ -496,6 +500,13 @@ moe_status moe_set_timing_events(hipEvent_t* events, int32_t n) {
   if (n < MOE_NUM_MARKS) return fail(MOE_ERR_INVALID_ARG, "need %d events, got %d", (int)MOE_NUM_MARKS, n);
   for (int i = 0; i < MOE_NUM_MARKS; ++i) g_marks[i] = events[i];
   g_marks_on = true;
+  return MOE_OK;
+}
+
+moe_status moe_route_margin(const moe_config* cfg, float* delta) {
+  MOE_TRY(check_cfg(cfg));
+  if (!delta) return fail(MOE_ERR_INVALID_ARG, "delta is NULL");
+  *delta = cfg->gate == MOE_GATE_SOFTMAX ? kRecheckDeltaSoftmax : kRecheckDeltaSigmoid;
   return MOE_OK;
 }
 

@@ -4,6 +4,8 @@
 // (s = Sigmoid(u_t^T e_i); expert i is selected when s_i + b_i is among the K largest keys, and its gate
 // is the raw s_i). Keys are compared in fp32; a token whose K-th and (K+1)-th keys are closer than
 // `delta` is selected again from fp64 logits, so the selected set is the exact top-K of the keys.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -225,6 +227,44 @@ void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s) {
   }
 }
 
+// ------------------------------------------------------------------ recheck margin per token
+// The fp32 logits round every partial sum of u_t . e_i; each rounding is proportional to the running sum,
+// which is at most |u_t| |e_i| (Cauchy-Schwarz). The base margin holds for |u_t| |e_i| up to sqrt(d) (token
+// rows of RMS 1 against centroids of norm 1); a token whose |u_t| max_i |e_i| is larger gets the margin
+// scaled by the ratio. wn2[i] = |e_i|^2, one block per routed expert.
+__global__ __launch_bounds__(256) void router_centroid_norms(const float* __restrict__ wg, int E, int d,
+                                                             float* __restrict__ wn2) {
+  __shared__ float part[4];
+  const int e = blockIdx.x;
+  float s = 0.f;
+  for (int k = threadIdx.x; k < d; k += 256) {
+    const float v = wg[(size_t)e * d + k];
+    s = fmaf(v, v, s);
+  }
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) wn2[e] = (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// delta * max(1, |u_t| max_i |e_i| / sqrt(d)) for the token row u_t, on one wave
+template <typename TU>
+__device__ __forceinline__ float token_margin(const TU* __restrict__ ut, int d, const float* __restrict__ wn2, int E,
+                                              float delta, int lane) {
+  float su = 0.f;
+  for (int k = lane; k < d; k += 64) {
+    float v;
+    if constexpr (sizeof(TU) == 2) v = bf16_to_f32(ut[k]);
+    else v = ut[k];
+    su = fmaf(v, v, su);
+  }
+  su = wave_sum(su);
+  float wm = 0.f;
+  for (int e = lane; e < E; e += 64) wm = fmaxf(wm, wn2[e]);
+  wm = wave_max(wm);
+  return delta * fmaxf(1.f, sqrtf(su * wm / (float)d));
+}
+
 // ------------------------------------------------------------------ top-K of one token per wave
 __device__ __forceinline__ float f32_unorder(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
@@ -313,10 +353,11 @@ __device__ __forceinline__ V group_limit_wave(const V key[4], bool valid[4], int
   return mth - m1;
 }
 
-template <int GATE>
+template <int GATE, typename TU>
 __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, int T, int E, int K,
                                                    const float* __restrict__ bias, int renorm, int G, int M,
-                                                   float delta,
+                                                   float delta, const TU* __restrict__ u, int d,
+                                                   const float* __restrict__ wn2,
                                                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                    int* __restrict__ recheck_count, int* __restrict__ recheck_list) {
   const int lane = threadIdx.x & 63;
@@ -383,7 +424,8 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, 
     topk_idx[(size_t)t * K + rank] = my_e;
     topk_w[(size_t)t * K + rank] = g;
   }
-  if (lane == 0 && gap < delta) {
+  const float margin = token_margin(u + (size_t)t * d, d, wn2, E, delta, lane);
+  if (lane == 0 && gap < margin) {
     const int pos = atomicAdd(recheck_count, 1);
     recheck_list[pos] = t;
   }
@@ -577,15 +619,24 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   hipError_t err = launch_router_logits(a, s);
   if (err != hipSuccess) return err;
+  router_centroid_norms<<<a.E, 256, 0, s>>>(a.wg, a.E, a.d, a.wn2);
   const int nb = cdiv(a.T, 4);
-  if (a.gate == MOE_GATE_SOFTMAX)
-    router_topk<MOE_GATE_SOFTMAX><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.n_groups, a.topk_groups,
-                                                     a.delta, a.topk_idx,
-                                                     a.topk_w, a.recheck_count, a.recheck_list);
-  else
-    router_topk<MOE_GATE_SIGMOID_BIAS><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.n_groups,
-                                                          a.topk_groups, a.delta, a.topk_idx,
-                                                          a.topk_w, a.recheck_count, a.recheck_list);
+  auto topk = [&](auto gate, auto* u) {
+    constexpr int G = decltype(gate)::value;
+    router_topk<G><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.n_groups, a.topk_groups, a.delta, u,
+                                      a.d, a.wn2, a.topk_idx, a.topk_w, a.recheck_count, a.recheck_list);
+  };
+  using Softmax = std::integral_constant<int, MOE_GATE_SOFTMAX>;
+  using Sigmoid = std::integral_constant<int, MOE_GATE_SIGMOID_BIAS>;
+  const uint16_t* ub = static_cast<const uint16_t*>(a.u);
+  const float* uf = static_cast<const float*>(a.u);
+  if (a.gate == MOE_GATE_SOFTMAX) {
+    if (a.u_bf16) topk(Softmax{}, ub);
+    else topk(Softmax{}, uf);
+  } else {
+    if (a.u_bf16) topk(Sigmoid{}, ub);
+    else topk(Sigmoid{}, uf);
+  }
   if (a.u_bf16)
     router_recheck_logits<uint16_t><<<a.E, kRecheckThreads, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.E, a.d,
                                                                      a.recheck_count, a.recheck_list, a.z64);

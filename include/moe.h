@@ -106,13 +106,19 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
  *  bias     [E] fp32 selection bias, used only with MOE_GATE_SIGMOID_BIAS (NULL = zeros).
  *  topk_idx [T, K] int32 out: the selected routed experts of each token in ascending expert order.
  *           Keys are compared in fp32 and every token whose K-th and (K+1)-th keys are closer than
- *           2e-4 (softmax: logit units) or 4e-5 (sigmoid + bias) is decided again from fp64 logits, so
- *           the set is the exact top-K; ties go to the lower expert index.
+ *           delta_t = delta * max(1, |u_t| max_i |e_i| / sqrt(d)) is decided again from fp64 logits, so
+ *           the set is the exact top-K; ties go to the lower expert index. delta (moe_route_margin) is
+ *           2e-4 for softmax (logit units) and 4e-5 for sigmoid + bias (key units); the factor scales it
+ *           with the size of the token's fp32 partial sums (|.| the Euclidean norm, e_i the rows of
+ *           w_gate).
  *  topk_w   [T, K] fp32 out: gates, same order. Softmax: the probability over all E routed experts
  *           (renormalised over the K selected when cfg->renorm). Sigmoid: the affinity s, never s + b
  *           (renormalised when cfg->renorm). */
 moe_status moe_route(const moe_config* cfg, const moe_layer* layer, const void* u, const float* bias,
                      int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The base recheck margin delta of moe_route for this configuration's gating (host output). */
+moe_status moe_route_margin(const moe_config* cfg, float* delta);
 
 /* The router's fp32 logits alone (the first step of moe_route; for diagnostics and tests):
  * z [T, E] fp32 out, z[t][i] = u_t . e_i + logit_offset[i], computed exactly as moe_route computes the
