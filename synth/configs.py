@@ -22,6 +22,7 @@ from . import gen
 
 STREAM_U, STREAM_WG, STREAM_BIAS, STREAM_ZIPF = 0, 1, 2, 3
 STREAM_SH_W1, STREAM_SH_W3, STREAM_SH_W2 = 4, 5, 6
+STREAM_U_TAIL = 7
 
 
 def stream_routed(e: int, which: int) -> int:
@@ -48,6 +49,7 @@ class Workload:
     gamma: Optional[float] = None   # bias update speed, when the workload includes one
     n_groups: int = 0               # group-limited routing: experts in n_groups groups, topk_groups kept
     topk_groups: int = 0
+    u_tail: bool = False            # heavy-tailed token rows (see tail_factors)
 
     @property
     def fs(self) -> int:
@@ -84,9 +86,26 @@ def sigma_down(w: Workload) -> float:
     return 1.0 / math.sqrt(w.f)
 
 
+def tail_factors(w: Workload) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Heavy tails for the token rows: word t of stream (seed, STREAM_U_TAIL) picks c = word % 16; c = 0
+    scales row t by 32, c = 1 or 2 by 8, and c = 3 scales the single element (word >> 8) % d by 64.
+    Returns (row factor [T] fp32, spiked rows, their spiked column)."""
+    wd = gen.words(gen.tensor_key(w.seed, STREAM_U_TAIL), 0, w.T)
+    c = (wd % np.uint64(16)).astype(np.int64)
+    row = np.where(c == 0, 32.0, np.where((c == 1) | (c == 2), 8.0, 1.0)).astype(np.float32)
+    spikes = np.flatnonzero(c == 3)
+    cols = ((wd[spikes] >> np.uint64(8)) % np.uint64(w.d)).astype(np.int64)
+    return row, spikes, cols
+
+
 def make_u(w: Workload) -> np.ndarray:
-    """u [T, d]: fp32 array for act f32, uint16 bf16 bit patterns for act bf16."""
+    """u [T, d]: fp32 array for act f32, uint16 bf16 bit patterns for act bf16 (heavy-tailed rows when
+    w.u_tail: the fp32 values scaled by tail_factors before the storage rounding)."""
     x = gen.normal_f32(w.seed, STREAM_U, (w.T, w.d), 1.0)
+    if w.u_tail:
+        row, spikes, cols = tail_factors(w)
+        x = (x * row[:, None]).astype(np.float32)
+        x[spikes, cols] = (x[spikes, cols] * np.float32(64.0)).astype(np.float32)
     return x if w.act == "f32" else gen.f32_to_bf16_bits(x)
 
 

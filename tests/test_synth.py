@@ -98,3 +98,17 @@ def test_workload_shapes_follow_the_pages():
     assert w2.f == b2["expert_size_vs_ffn"] * 4 * w2.d
     b16, w3 = g["dsmoe_16b"]["value"], configs.WORKLOADS["dsmoe16b_bf16"]
     assert (w3.Ks, w3.E, w3.K, w3.d) == (b16["shared"], b16["routed"], b16["active_routed"], b16["hidden"])
+
+
+def test_heavy_tailed_rows_are_exact_power_of_two_scalings():
+    # u_tail scales whole rows by 32 or 8 and single elements by 64 (powers of two: exact in fp32), from
+    # the words of their own stream; the rest of u is the plain draw
+    w = configs.WORKLOADS["tiny_f32"].replace(T=400, u_tail=True)
+    plain = configs.make_u(w.replace(u_tail=False))
+    tail = configs.make_u(w)
+    row, spikes, cols = configs.tail_factors(w)
+    expect = plain * row[:, None]
+    expect[spikes, cols] *= 64.0
+    assert np.array_equal(tail, expect)
+    assert 0.03 < (row == 32).mean() < 0.1 and 0.08 < (row == 8).mean() < 0.2 and 0.03 < len(spikes) / w.T < 0.1
+    assert np.array_equal(configs.tail_factors(w)[0], row)          # a pure function of (seed, T)
