@@ -27,6 +27,18 @@ def err(y, y_ref) -> float:
     return float(np.abs(y - y_ref).max() / max(rms, 1e-300))
 
 
+def err_rows(y, y_ref, slack=0.0) -> float:
+    """max over rows of max(|y_r - y_ref_r| - slack_r) / RMS(y_ref_r): the tolerance applied row by row, for
+    inputs whose rows differ in scale by orders of magnitude (heavy-tailed tokens), where one global RMS
+    would let the large rows hide the small ones and hold the large ones to the small ones' scale. slack
+    (per element, or 0) is the output format's own rounding, which an element far above its row's RMS
+    carries in full (bf16 rounds by up to 2^-9 of the value)."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    rms = np.sqrt(np.mean(y_ref ** 2, axis=1))
+    return float((np.maximum(np.abs(y - y_ref) - slack, 0.0).max(axis=1) / np.maximum(rms, 1e-300)).max())
+
+
 def to_np(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu()
     if t.dtype == torch.bfloat16:
@@ -193,3 +205,31 @@ def oracle_route(g: GpuLayer):
     w = g.w
     z = omoe.router_logits(g.u_host, g.wg, g.off)
     return z, omoe.route(z, w.gate, w.K, g.bias, w.renorm)
+
+
+def token_margins(cfg, u_host: np.ndarray, wg: np.ndarray) -> np.ndarray:
+    """The router's recheck margin of every token, as the header states it:
+    delta * max(1, |u_t| max_i |e_i| / sqrt(d)), delta from the library (moe_route_margin)."""
+    delta = moe.moe_route_margin(cfg)
+    un = np.sqrt((np.asarray(u_host, dtype=np.float64) ** 2).sum(axis=1))
+    wn = np.sqrt((np.asarray(wg, dtype=np.float64) ** 2).sum(axis=1)).max()
+    return delta * np.maximum(1.0, un * wn / np.sqrt(u_host.shape[1]))
+
+
+def check_key_margins(g, z32: np.ndarray, ref_key: np.ndarray, gap: np.ndarray, label: str = "") -> None:
+    """The fp32 keys the router compares stay 20x inside each token's recheck margin (so every token whose
+    selection the fp32 keys could get wrong is decided again in fp64), and no fp64 near-tie makes the
+    selection ill-defined."""
+    w = g.w
+    bias = g.bias if (w.gate == "sigmoid_bias" and g.bias is not None) else None
+    key32 = 1.0 / (1.0 + np.exp(-z32.astype(np.float64))) if w.gate == "sigmoid_bias" else z32.astype(np.float64)
+    key64 = ref_key - (bias[None, :] if bias is not None else 0.0)
+    kerr = np.abs(key32 - key64).max(axis=1)
+    margin = token_margins(g.cfg, g.u_host, g.wg)
+    worst = float((kerr * 20 / margin).max())
+    print(f"{label}: max fp32 key error {kerr.max():.3e}, worst 20 x error / margin {worst:.3f}, margin "
+          f"{margin.min():.2e}..{margin.max():.2e}, min fp64 gap {gap.min():.3e}, tokens under their margin "
+          f"{int((gap < margin).sum())}", flush=True)
+    assert worst <= 1.0, "fp32 keys are not 20x inside the recheck margin"
+    assert gap.min() > 1e-9, "an fp64 near-tie would make the selection ill-defined"
+

@@ -48,6 +48,13 @@ SMALL = {
     # inner dim 512: with d = 1024 and f = 128 the bf16 rounding of the routed sum reaches the tolerance)
     "bf16_mfma_router_e63": W["dsmoe2b_bf16"].replace(name="bf16_mfma_router_e63", T=2100, d=1024, E=63, K=7,
                                                        f=512),
+    # heavy-tailed token rows (about 1 in 16 scaled by 32, 1 in 8 by 8, 1 in 16 with one element scaled by
+    # 64): the 1x128 amax, the requantization and the router's recheck margins on outliers; the MFMA
+    # router logits and the vector-ALU logits, E4M3 and bf16 experts. Rows then differ in scale by up to
+    # 32^2 (SwiGLU is quadratic in u), so the tolerance is applied row by row (H.err_rows).
+    "fp8_heavy_tail": W["v3_fp8"].replace(name="fp8_heavy_tail", T=300, d=512, E=20, K=4, u_tail=True),
+    "bf16_heavy_tail_mfma_router": W["dsmoe2b_bf16"].replace(name="bf16_heavy_tail_mfma_router", T=2100, d=1024,
+                                                             E=63, K=7, f=512, u_tail=True),
 }
 
 
@@ -66,6 +73,14 @@ def _oracle_layer(g):
 def _check_all(g, o, ref):
     w = g.w
     tol = H.TOL[w.wdt]
+    y_bf16 = o["y_r"].dtype == torch.bfloat16
+    gw = H.to_np(o["gw"])
+
+    def err(y, y_ref, rounding=None):
+        # heavy-tailed rows: the tolerance row by row, past the bf16 rounding of each stored element
+        if not w.u_tail:
+            return H.err(y, y_ref)
+        return H.err_rows(y, y_ref, 0.0 if rounding is None else 2.0 ** -8 * rounding)
     assert np.array_equal(H.to_np(o["idx"]), ref["idx"]), "routing differs"
     assert np.array_equal(H.to_np(o["counts"]), ref["counts"])
     assert np.array_equal(H.to_np(o["offsets"]), ref["offsets"])
@@ -73,29 +88,37 @@ def _check_all(g, o, ref):
     assert np.array_equal(H.to_np(o["row_of"]), ref["row_of"])
     gate_err = np.abs(H.to_np(o["gw"]) - ref["w"]).max()
     assert gate_err < 1e-5, gate_err
-    e_rows = H.err(H.to_np(o["y_r"]), ref["y_rows"])
+    e_rows = err(H.to_np(o["y_r"]), ref["y_rows"], np.abs(ref["y_rows"]) if y_bf16 else None)
     assert e_rows <= tol, f"per-row expert outputs err {e_rows}"
     if w.Ks > 0:
-        e_sh = H.err(H.to_np(o["y_s"]), ref["y_shared"])
+        e_sh = err(H.to_np(o["y_s"]), ref["y_shared"], np.abs(ref["y_shared"]) if y_bf16 else None)
         assert e_sh <= tol, f"shared err {e_sh}"
-    gw = H.to_np(o["gw"])
     y = H.to_np(o["y_r"])
-    routed = omoe.combine(np.zeros_like(g.u_host), np.zeros_like(g.u_host), y, ref["row_of"], gw)
-    e_routed = H.err(routed, ref["routed"])
+    zero = np.zeros_like(g.u_host)
+    routed = omoe.combine(zero, zero, y, ref["row_of"], gw)
+    routed_mag = omoe.combine(zero, zero, np.abs(ref["y_rows"]), ref["row_of"], np.abs(gw)) if y_bf16 else None
+    e_routed = err(routed, ref["routed"], routed_mag)
     assert e_routed <= tol, f"routed sum err {e_routed}"
-    e_h = H.err(H.to_np(o["h"]), ref["h"])
+    h_bf16 = o["h"].dtype == torch.bfloat16
+    e_h = err(H.to_np(o["h"]), ref["h"], np.abs(ref["h"]) if h_bf16 else None)
     assert e_h <= tol, f"h err {e_h}"
     return dict(rows=e_rows, h=e_h, routed=e_routed)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_layer_stages_match_oracle(name):
+    import fine_grained_mixture_gemm_amd as moe
     print(f"[case] {name}", flush=True)
     g = H.build(SMALL[name])
     ws = H.workspace(g, poison=True)
     o = H.run_stages(g, ws)
     ref = _oracle_layer(g)
     errs = _check_all(g, o, ref)
+    z = torch.empty((g.w.T, g.w.E), dtype=torch.float32, device="cuda")
+    moe.moe_router_logits(g.cfg, g.layer, g.t["u"], z, ws)
+    torch.cuda.synchronize()
+    r = omoe.route(ref["z"], g.w.gate, g.w.K, g.bias, g.w.renorm, g.w.n_groups, g.w.topk_groups)
+    H.check_key_margins(g, H.to_np(z), r["key"], r["gap"], name)
     print(name, errs)
 
 
@@ -129,10 +152,67 @@ def test_full_size_float_configs(name):
     ws = H.workspace(g)
     o = H.run_stages(g, ws)
     ref = _oracle_layer(g)
-    # the fp32 logits (softmax keys) stay 20x inside the 2e-4 recheck margin
+    # the fp32 logits (softmax keys) stay 20x inside every token's recheck margin
     z = torch.empty((g.w.T, g.w.E), dtype=torch.float32, device="cuda")
     moe.moe_router_logits(g.cfg, g.layer, g.t["u"], z, ws)
     torch.cuda.synchronize()
-    kerr = float(np.abs(H.to_np(z) - ref["z"]).max())
-    print(name, "min gap", float(ref["gap"].min()), "fp32 logit error", kerr, _check_all(g, o, ref))
-    assert kerr * 20 <= 2e-4
+    r = omoe.route(ref["z"], g.w.gate, g.w.K, g.bias, g.w.renorm, g.w.n_groups, g.w.topk_groups)
+    H.check_key_margins(g, H.to_np(z), r["key"], r["gap"], name)
+    print(name, _check_all(g, o, ref))
+
+
+# E4M3 with the smallest inner dim f = 128: a row of a is one 1x128 tile, so one requantized code of a
+# that rounds the other way moves that row of y by about 0.3 * 3 / sqrt(128) = 8 % of its RMS, above the
+# 6e-2 bar. Such a code is one whose input window (the gate/up GEMM's fp32 summation bound carried through
+# SwiGLU, tests/e4m3_bounds.py) crosses a rounding midpoint or can move its tile's scale; the check
+# compares per element |y - y_ref| <= 6e-2 RMS + 2^-8 |y_ref| (bf16 output) + sum_c |W2[i, c]| flip_a[r, c],
+# and bounds the rest with the RMS error (<= 1e-2) and the plain maximum (<= 0.25 of the RMS).
+F128 = {
+    "fp8_f128_tiled": W["v3_fp8"].replace(name="fp8_f128_tiled", T=300, d=512, E=12, K=3, f=128),
+    "fp8_f128_decode": W["v3_fp8"].replace(name="fp8_f128_decode", T=64, d=512, E=12, K=3, f=128),
+}
+
+
+def _flip_aware(y_gpu, y_ref, x, ex, what):
+    from oracle import quant as oquant
+    from tests import e4m3_bounds as EB
+    (_, _, _, _), (a32, Da) = EB.forward_windows(x, ex[0], ex[1])
+    code, scale = EB.flip(a32, Da, axis_tiles=1, parts=True)                # [n, f]
+    flip_a = code + scale
+    w2 = np.abs(oquant.dequant_weight(ex[2], ex[3]))                        # [d, f]
+    allow = flip_a @ w2.T                                                   # [n, d]
+    rms = np.sqrt(np.mean(y_ref ** 2))
+    diff = np.abs(y_gpu - y_ref)
+    excess = (diff - (H.TOL["fp8"] * rms + 2.0 ** -8 * np.abs(y_ref) + allow)).max() / rms
+    rms_err, plain = np.sqrt(np.mean(diff ** 2)) / rms, diff.max() / rms
+    assert excess <= 0, f"{what}: exceeds the flip-aware bound by {excess:.4f} RMS (plain {plain:.4f})"
+    assert rms_err <= 1e-2 and plain <= 0.25, f"{what}: RMS error {rms_err:.4f}, plain {plain:.4f}"
+    return plain, int((code > 0).sum())
+
+
+@pytest.mark.parametrize("name", list(F128))
+def test_fp8_inner_dim_128_flip_aware(name):
+    w = F128[name]
+    print(f"[case] {name}", flush=True)
+    g = H.build(w)
+    ws = H.workspace(g, poison=True)
+    o = H.run_stages(g, ws)
+    z = omoe.router_logits(g.u_host, g.wg, g.off)
+    r = omoe.route(z, w.gate, w.K, g.bias, w.renorm)
+    assert np.array_equal(H.to_np(o["idx"]), r["idx"]), "routing differs"
+    offsets, perm, _ = omoe.dispatch(r["idx"], w.E)
+    assert np.array_equal(H.to_np(o["offsets"]), offsets) and np.array_equal(H.to_np(o["perm"]), perm)
+    y = H.to_np(o["y_r"])
+    worst, flips = 0.0, 0
+    for e in range(w.E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        ex = H.oracle_fp8_expert(w, e)
+        x = g.u_host[perm[a:b]]
+        p, nf = _flip_aware(y[a:b], omoe.swiglu_ffn_fp8(x, *ex)[0], x, ex, f"{name} expert {e}")
+        worst, flips = max(worst, p), flips + nf
+    ex = H.oracle_fp8_expert(w, -1)
+    p, nf = _flip_aware(H.to_np(o["y_s"]), omoe.swiglu_ffn_fp8(g.u_host, *ex)[0], g.u_host, ex, f"{name} shared")
+    worst, flips = max(worst, p), flips + nf
+    print(f"{name}: worst plain max-abs/RMS {worst:.4f}, codes of a that may round either way {flips}")
