@@ -8,8 +8,10 @@ the V3-shaped layer: T = 8192 tokens, d = 7168, 1 shared + 256 routed SwiGLU exp
 sigmoid affinity + selection bias, top-8, renormalised gates, E4M3 experts with 1x128 / 128x128 scales.
 
 Prints ONE JSON line. `roofline` covers the dominant kernel (the gate/up grouped GEMM), timed live with
-HIP events on the launch stream over the timed steps; `cpu_baseline` times the float64 CPU oracle on a
-bounded sample of the same workload on this host.
+HIP events on the launch stream over the timed steps; `configs` holds the same record for the other
+configurations (the 2B and 16B bf16 layers and the 64-token V3 decode step), each timed in a run of its
+own after the headline; `cpu_baseline` times the float64 CPU oracle on a bounded sample of the headline
+workload on this host, scaled to the whole batch.
 """
 from __future__ import annotations
 
@@ -28,18 +30,26 @@ METRIC = "MoE layer tokens/sec + grouped-GEMM TFLOPS (% MFMA peak), V3-shaped la
 PEAK = {"fp8": 5.0e15, "bf16": 2.5e15, "f32": 157.3e12, "hbm": 8.0e12}
 
 
+def note(msg):
+    """Progress on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="v3_fp8")
     ap.add_argument("--tokens", type=int, default=0,
                     help="run the workload's layer with this many tokens instead (a sweep over batch sizes; the "
                          "workload name gains a _t<T> suffix and no profiled traffic is attached)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the E4M3 expert backward")
-    ap.add_argument("--cpu-tokens", type=int, default=1, help="tokens of the workload the oracle runs")
+    ap.add_argument("--no-subconfigs", action="store_true",
+                    help="skip the timed runs of the other configurations (2B / 16B bf16 layers, V3 decode step)")
+    ap.add_argument("--sub-steps", type=int, default=200)
+    ap.add_argument("--sub-warmup", type=int, default=20)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size kernel that profiler "
                          "counters of HBM traffic are scaled against)")
@@ -217,52 +227,168 @@ def cpu_model():
     return platform.processor()
 
 
-def cpu_baseline(w, n_tokens):
-    """The float64 oracle on the first n_tokens tokens of the workload (their routed experts and the
-    shared block). Weight generation and E4M3 weight quantization are set-up and are not timed."""
+def cpu_baseline(w, repeats=3):
+    """The float64 oracle on a bounded sample of the workload's layer, scaled to the whole batch.
+
+    Timed on the host, median of `repeats` runs: the router (logits, gating, top-K) and dispatch on all T
+    tokens, four routed experts on their own rows (the fewest rows, the most, and two between, by rank
+    in load), and the combine on all T tokens. The oracle's expert costs a fixed part (turning E4M3
+    weights into float64) plus a part per row; the least-squares line through the four timed experts gives
+    every other routed expert's time and the shared block's (inner dim Ks*f, scaled by Ks). Weight
+    generation and quantization are set-up, not timed."""
     import numpy as np
     from oracle import moe as omoe, quant as oquant
-    from synth import configs
+    from synth import configs, gen
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    ws = w.replace(T=n_tokens)
-    u = configs.u_as_f32(ws, configs.make_u(ws))
-    wg, bias, off = configs.make_router(ws)
-    r = omoe.route(omoe.router_logits(u, wg, off), ws.gate, ws.K, bias, ws.renorm)
-    need = sorted(set(int(e) for e in r["idx"].reshape(-1)))
-    experts = [None] * ws.E
+    u = configs.u_as_f32(w, configs.make_u(w))
+    wg, bias, off = configs.make_router(w)
 
     def weights(e):
-        w1, w3, w2 = configs.master_w1(ws, e), configs.master_w3(ws, e), configs.master_w2(ws, e)
-        if ws.wdt == "fp8":
+        w1, w3, w2 = configs.master_w1(w, e), configs.master_w3(w, e), configs.master_w2(w, e)
+        if w.wdt == "fp8":
             return (*oquant.quantize_weight_128x128(np.vstack([w1, w3])), *oquant.quantize_weight_128x128(w2))
-        if ws.wdt == "bf16":
-            from synth import gen
+        if w.wdt == "bf16":
             st = lambda x: gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(x))
             return st(w1), st(w3), st(w2)
         return w1, w3, w2
 
-    t0 = time.time()
-    for e in need:
-        experts[e] = weights(e)
-    shared = weights(-1) if ws.Ks > 0 else None
-    setup = time.time() - t0
-    runs, t_run = 0, 0.0
-    while runs < 3 and (runs == 0 or t_run < 10.0):
-        t1 = time.perf_counter()
-        omoe.layer_forward(u, wg, experts, shared, gate=ws.gate, K=ws.K, bias=bias, renorm=ws.renorm,
-                           logit_offset=off, fp8=(ws.wdt == "fp8"))
-        t_run += time.perf_counter() - t1
-        runs += 1
-    per = t_run / runs
-    return {"value": round(n_tokens / per, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"first {n_tokens} token(s) of the {w.name} workload through the float64 oracle layer "
-                       f"(their {len(need)} routed experts + the shared block), mean of {runs} run(s), "
-                       f"{per:.2f} s each; weight generation/quantization ({setup:.0f} s) untimed; "
-                       f"host: {cpu_model()}")}
+    def ffn(x, ex):
+        if w.wdt == "fp8":
+            return omoe.swiglu_ffn_fp8(x, *ex)[0]
+        return omoe.swiglu_ffn(x, *ex)
+
+    r = omoe.route(omoe.router_logits(u, wg, off), w.gate, w.K, bias, w.renorm)
+    offsets, perm, row_of = omoe.dispatch(r["idx"], w.E)
+    rows = np.diff(offsets)
+    touched = np.flatnonzero(rows)
+    by_load = touched[np.argsort(rows[touched], kind="stable")]
+    sample = [int(by_load[round(q * (len(by_load) - 1))]) for q in (0.0, 1 / 3, 2 / 3, 1.0)]
+    ex = {e: weights(e) for e in sample}
+    y_rows = np.zeros((w.T * w.K, w.d))
+    runs = []
+    for _ in range(repeats):
+        t = {}
+        t0 = time.perf_counter()
+        r = omoe.route(omoe.router_logits(u, wg, off), w.gate, w.K, bias, w.renorm)
+        offsets, perm, row_of = omoe.dispatch(r["idx"], w.E)
+        t["route"] = time.perf_counter() - t0
+        for e in sample:
+            t0 = time.perf_counter()
+            y_rows[offsets[e]:offsets[e + 1]] = ffn(u[perm[offsets[e]:offsets[e + 1]]], ex[e])
+            t[e] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        omoe.combine(u, np.zeros_like(u), y_rows, row_of, r["w"])
+        t["combine"] = time.perf_counter() - t0
+        per_row, fixed = np.polyfit([float(rows[e]) for e in sample], [t[e] for e in sample], 1)
+        per_row, fixed = max(float(per_row), 0.0), max(float(fixed), 0.0)
+        routed = fixed * len(touched) + per_row * float(rows.sum())
+        shared = w.Ks * (fixed + per_row * w.T) if w.Ks > 0 else 0.0
+        total = t["route"] + routed + shared + t["combine"]
+        runs.append((total, t["route"] + sum(t[e] for e in sample) + t["combine"], fixed, per_row))
+        note(f"cpu baseline run {len(runs)}/{repeats}: {runs[-1][1]:.1f} s timed, {total:.0f} s for the batch")
+    runs.sort()
+    total, timed, fixed, per_row = runs[len(runs) // 2]
+    return {"value": round(w.T / total, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{w.name} (T = {w.T}) through the float64 oracle, median of {repeats} runs: router and "
+                       f"dispatch on all tokens, routed experts "
+                       f"{', '.join(f'{e} ({int(rows[e])} rows)' for e in sample)} on their rows, combine on "
+                       f"all tokens ({timed:.1f} s timed per run); the other {len(touched) - len(sample)} "
+                       f"touched experts and the shared block from the least-squares line through those "
+                       f"({fixed:.2f} s + {per_row * 1e3:.2f} ms per row), {total:.0f} s "
+                       f"for the whole batch; weight generation/quantization untimed; host: {cpu_model()}")}
+
+
+def library_record(moe):
+    import hashlib
+    return {"path": os.path.relpath(moe.LIB_PATH, ROOT),
+            "sha256": hashlib.sha256(open(moe.LIB_PATH, "rb").read()).hexdigest()[:16]}
+
+
+def measure(moe, layers, w, steps, warmup):
+    """Build workload w on the device and time `steps` steps after `warmup` untimed ones. Returns the
+    record (step time, per-stage times from HIP events on the launch stream, grouped-GEMM rates and
+    rooflines) and the device layer, workspace and step outputs for further timings."""
+    import ctypes
+    import torch
+    t_setup = time.time()
+    L = layers.device_layer(w)
+    setup_s = time.time() - t_setup
+    ws = torch.empty(moe.moe_workspace_size(L.cfg), dtype=torch.uint8, device="cuda")
+    h = torch.empty_like(L.t["u"])
+    idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    bias = L.t["bias"]
+    bias_next = bias.clone() if w.gamma is not None else None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        # every step routes with the workload's bias and makes one update of it (into bias_next), so the
+        # routing, and with it the work, is the same in every step
+        moe.moe_forward(L.cfg, L.layer, L.t["u"], bias, h, idx, counts, ws)
+        if w.gamma is not None:
+            bias_next.copy_(bias)
+            moe.moe_update_bias(L.cfg, counts, w.gamma, bias_next)
+
+    # stage events: one set per timed step, created by recording them once
+    marks = []
+    for _ in range(steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_MARKS)]
+        for e in evs:
+            e.record(stream)
+        marks.append(evs)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(steps):
+        arr = (ctypes.c_void_p * moe.MOE_NUM_MARKS)(*[e.cuda_event for e in marks[i]])
+        moe.moe_set_timing_events(arr)
+        step()
+    moe.moe_set_timing_events(None)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / steps
+    stage = {}
+    for a, b in zip(moe.MARK_NAMES[:-1], moe.MARK_NAMES[1:]):
+        ia, ib = moe.MARK_NAMES.index(a), moe.MARK_NAMES.index(b)
+        stage[b.replace("_end", "")] = sum(m[ia].elapsed_time(m[ib]) for m in marks) / steps
+    gwork, dwork, touched = kernel_work(w, counts.cpu().numpy())
+    peak = PEAK[w.wdt]
+    gemm_ms = stage["gateup"] + stage["down"]
+    gemm_tflops = (gwork["flops"] + dwork["flops"]) / (gemm_ms * 1e-3) / 1e12
+    rec = {
+        "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 4), "dtype": {"fp8": "fp8_e4m3", "bf16": "bf16", "f32": "f32"}[w.wdt],
+        "config": {"workload": w.name, "T": w.T, "d_model": w.d, "routed": w.E, "shared": w.Ks, "top_k": w.K,
+                   "inter_dim": w.f, "gate": w.gate, "renorm": w.renorm, "weights": w.wdt, "act": w.act,
+                   "bias_update": w.gamma is not None},
+        "roofline": dict(kernel=gateup_kernel_name(w), **roofline(gwork, stage["gateup"], peak)),
+        "algorithmic_bytes": {"gateup": int(gwork["bytes"]), "down": int(dwork["bytes"])},
+        "algorithmic_flops": {"gateup": gwork["flops"], "down": dwork["flops"]},
+        "grouped_gemm_tflops": round(gemm_tflops, 1),
+        "grouped_gemm_mfma_frac": round(gemm_tflops * 1e12 / peak, 4),
+        "grouped_gemm_hbm_gbps": round((gwork["bytes"] + dwork["bytes"]) / (gemm_ms * 1e-3) / 1e9, 1),
+        "grouped_gemm_hbm_frac": round((gwork["bytes"] + dwork["bytes"]) / (gemm_ms * 1e-3) / PEAK["hbm"], 4),
+        "down_roofline": roofline(dwork, stage["down"], peak),
+        "stages_ms": {k: round(v, 4) for k, v in stage.items()},
+        "touched_experts": touched,
+        "setup_s": round(setup_s, 1),
+    }
+    prof = profiled_traffic(w.name)
+    if prof is not None:
+        rec["roofline"]["traffic"] = round(prof["gateup"]["traffic_bytes"])
+        rec["down_roofline"]["traffic"] = round(prof["down"]["traffic_bytes"])
+    note(f"{w.name}: {ms:.3f} ms per step over {steps} steps, gate/up {stage['gateup']:.3f} ms, "
+         f"down {stage['down']:.3f} ms (set-up {setup_s:.0f} s)")
+    return rec, L, ws
+
+
+SUB_WORKLOADS = ("dsmoe2b_bf16", "dsmoe16b_bf16", "v3_fp8_decode")
 
 
 def main():
@@ -290,78 +416,33 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    t_setup = time.time()
-    L = layers.device_layer(w)
-    setup_s = time.time() - t_setup
-    ws = torch.empty(moe.moe_workspace_size(L.cfg), dtype=torch.uint8, device="cuda")
-    h = torch.empty_like(L.t["u"])
-    idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
-    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
-    bias = L.t["bias"].clone() if L.t["bias"] is not None else None
-    stream = torch.cuda.current_stream()
-
-    def step():
-        moe.moe_forward(L.cfg, L.layer, L.t["u"], bias, h, idx, counts, ws)
-        if w.gamma is not None:
-            moe.moe_update_bias(L.cfg, counts, w.gamma, bias)
-
-    # stage events: one set per timed step, created by recording them once
-    import ctypes
-    marks = []
-    for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(moe.MOE_NUM_MARKS)]
-        for e in evs:
-            e.record(stream)
-        marks.append(evs)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(args.steps):
-        arr = (ctypes.c_void_p * moe.MOE_NUM_MARKS)(*[e.cuda_event for e in marks[i]])
-        moe.moe_set_timing_events(arr)
-        step()
-    moe.moe_set_timing_events(None)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms = total_ms / args.steps
-    stage = {}
-    for a, b in zip(moe.MARK_NAMES[:-1], moe.MARK_NAMES[1:]):
-        ia, ib = moe.MARK_NAMES.index(a), moe.MARK_NAMES.index(b)
-        stage[b.replace("_end", "")] = sum(m[ia].elapsed_time(m[ib]) for m in marks) / args.steps
-    counts_h = counts.cpu().numpy()
-    gwork, dwork, touched = kernel_work(w, counts_h)
-    peak = PEAK[w.wdt]
-    gemm_ms = stage["gateup"] + stage["down"]
-    gemm_tflops = (gwork["flops"] + dwork["flops"]) / (gemm_ms * 1e-3) / 1e12
-    out = {
-        "metric": METRIC, "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": {"fp8": "fp8_e4m3", "bf16": "bf16", "f32": "f32"}[w.wdt],
-        "data": "synthetic",
-        "config": {"workload": w.name, "T": w.T, "d_model": w.d, "routed": w.E, "shared": w.Ks, "top_k": w.K,
-                   "inter_dim": w.f, "gate": w.gate, "renorm": w.renorm, "weights": w.wdt, "act": w.act,
-                   "bias_update": w.gamma is not None},
-        "roofline": dict(kernel=gateup_kernel_name(w), **roofline(gwork, stage["gateup"], peak)),
-        "algorithmic_bytes": {"gateup": int(gwork["bytes"]), "down": int(dwork["bytes"])},
-        "grouped_gemm_tflops": round(gemm_tflops, 1),
-        "grouped_gemm_mfma_frac": round(gemm_tflops * 1e12 / peak, 4),
-        "down_roofline": roofline(dwork, stage["down"], peak),
-        "stages_ms": {k: round(v, 4) for k, v in stage.items()},
-        "touched_experts": touched,
-        "setup_s": round(setup_s, 1),
-    }
+    rec, L, ws = measure(moe, layers, w, args.steps, args.warmup)
+    out = {"metric": METRIC, "value": rec.pop("value"), "unit": rec.pop("unit"), "n_gpus": 1,
+           "steps": rec.pop("steps"), "warmup": rec.pop("warmup"), "ms_per_step": rec.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": rec.pop("dtype"),
+           "data": "synthetic", "config": rec.pop("config")}
+    out.update(rec)
+    out["library"] = library_record(moe)
     out["balance_stats"] = time_balance_stats(moe, L, w, ws)
     if w.wdt == "fp8" and not args.no_backward:
         out["backward"] = time_backward(moe, L, w, ws)
-    prof = profiled_traffic(w.name)
-    if prof is not None:
-        out["roofline"]["traffic"] = round(prof["gateup"]["traffic_bytes"])
-        out["down_roofline"]["traffic"] = round(prof["down"]["traffic_bytes"])
+        note(f"expert backward: input {out['backward']['ms_input']} ms, input + weight "
+             f"{out['backward']['ms_input_and_weight']} ms")
+    del L, ws
+    torch.cuda.empty_cache()
+    if not args.no_subconfigs and args.tokens == 0:
+        # the other configurations the headline is quoted beside: the 2B and 16B bf16 layers (matrix-core
+        # bound at large batch) and the 64-token V3 decode step (a weight stream), each its own timed run
+        out["configs"] = {}
+        for name in SUB_WORKLOADS:
+            if name == w.name:
+                continue
+            sub, Ls, wss = measure(moe, layers, configs.WORKLOADS[name], args.sub_steps, args.sub_warmup)
+            out["configs"][name] = sub
+            del Ls, wss
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
 
 
