@@ -18,6 +18,8 @@ __all__ = [
     "moe_quantize_act", "moe_last_error", "moe_set_timing_events", "MOE_NUM_MARKS", "MARK_NAMES", "LIB_PATH",
     "moe_balance_stats", "moe_backward_workspace_size", "moe_expert_ffn_backward_input", "moe_transpose_fp8_weights",
     "moe_expert_ffn_backward", "moe_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES", "moe_route_margin",
+    "moe_pack_weights", "MOE_LAYOUT_ROWS", "MOE_LAYOUT_TILED", "MOE_PACK_W13", "MOE_PACK_W2", "MOE_PACK_WS13",
+    "MOE_PACK_WS2",
 ]
 
 # always the in-tree build, next to this file
@@ -29,6 +31,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS = range(2)
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = range(2)
+MOE_PACK_W13, MOE_PACK_W2, MOE_PACK_WS13, MOE_PACK_WS2 = range(4)
 MARK_NAMES = ("route_begin", "route_end", "dispatch_end", "quant_end", "gateup_end", "down_end", "combine_end")
 MOE_NUM_MARKS = len(MARK_NAMES)
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
@@ -42,7 +46,7 @@ class moe_config(ctypes.Structure):
 
 class moe_layer(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w13", "w2", "w13_scale", "w2_scale", "ws13", "ws2", "ws13_scale",
-                                                 "ws2_scale", "w_gate", "logit_offset")]
+                                                 "ws2_scale", "w_gate", "logit_offset")] + [("weight_layout", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -69,6 +73,7 @@ _SIGS = {
     "moe_expert_ffn_backward_input": [_CP, _LP, _LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "moe_expert_ffn_backward": [_CP, _LP, _LP] + [_vp] * 12 + [_sz, _vp],
     "moe_transpose_fp8_weights": [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp],
+    "moe_pack_weights": [_CP, _i32, _vp, _vp, _vp],
     "moe_quantize_weights": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
     "moe_quantize_act": [_vp, _i32, _i32, _i32, _vp, _vp, _vp],
     "moe_set_timing_events": [_vp, _i32],
@@ -114,10 +119,14 @@ def make_config(T, d_model, n_routed, n_shared, top_k, inter_dim, gate, renorm, 
 
 
 def make_layer(w13, w2, w_gate, ws13=None, ws2=None, w13_scale=None, w2_scale=None, ws13_scale=None,
-               ws2_scale=None, logit_offset=None) -> moe_layer:
+               ws2_scale=None, logit_offset=None, weight_layout=0) -> moe_layer:
     """Build the weight struct; the caller keeps the tensors alive while the struct is used."""
     return moe_layer(_dev(w13), _dev(w2), _dev(w13_scale), _dev(w2_scale), _dev(ws13), _dev(ws2), _dev(ws13_scale),
-                     _dev(ws2_scale), _dev(w_gate), _dev(logit_offset))
+                     _dev(ws2_scale), _dev(w_gate), _dev(logit_offset), int(weight_layout))
+
+
+def moe_pack_weights(cfg, which, src, dst, stream=None):
+    _call("moe_pack_weights", ctypes.byref(cfg), int(which), _dev(src), _dev(dst), _stream(stream))
 
 
 def moe_workspace_size(cfg) -> int:

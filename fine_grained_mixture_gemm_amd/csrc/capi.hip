@@ -324,6 +324,10 @@ moe_status check_layer_router(const moe_layer* l) {
 moe_status check_layer_experts(const moe_config* c, const moe_layer* l) {
   if (!l) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
   if (!l->w13 || !l->w2) return fail(MOE_ERR_INVALID_ARG, "layer->w13 / w2 is NULL");
+  if (l->weight_layout != MOE_LAYOUT_ROWS && l->weight_layout != MOE_LAYOUT_TILED)
+    return fail(MOE_ERR_INVALID_ARG, "bad weight_layout %d", l->weight_layout);
+  if (l->weight_layout == MOE_LAYOUT_TILED && c->w_dtype == MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "the tiled weight layout is for bf16 and fp8 weights");
   const bool fp8 = c->w_dtype == MOE_FP8_E4M3;
   if (fp8 && (!l->w13_scale || !l->w2_scale)) return fail(MOE_ERR_INVALID_ARG, "fp8 weights need w13_scale and w2_scale");
   if (c->n_shared > 0) {
@@ -421,6 +425,7 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   g.mt_prefix = mt_prefix;
   g.xrange = xrange;
   g.xcount = xcount;
+  g.packed = l->weight_layout == MOE_LAYOUT_TILED;
   const uint8_t* xin = static_cast<const uint8_t*>(u);
   const float* xs = nullptr;
   if (fp8) {
@@ -704,6 +709,28 @@ moe_status moe_backward_workspace_size(const moe_config* cfg, size_t* bytes) {
   return MOE_OK;
 }
 
+moe_status moe_pack_weights(const moe_config* cfg, int32_t which, const void* src, void* dst, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->w_dtype == MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "the tiled weight layout is for bf16 and fp8 weights");
+  const int esz = cfg->w_dtype == MOE_FP8_E4M3 ? 1 : 2;
+  const int E = cfg->n_routed, d = cfg->d_model, f = cfg->inter_dim, fs = cfg->n_shared * f;
+  int groups = 0, rows = 0, cols = 0;
+  bool gateup = false;
+  switch (which) {
+    case MOE_PACK_W13: groups = E; rows = 2 * f; cols = d; gateup = true; break;
+    case MOE_PACK_W2: groups = E; rows = d; cols = f; break;
+    case MOE_PACK_WS13: groups = fs > 0 ? 1 : 0; rows = 2 * fs; cols = d; gateup = true; break;
+    case MOE_PACK_WS2: groups = fs > 0 ? 1 : 0; rows = d; cols = fs; break;
+    default: return fail(MOE_ERR_INVALID_ARG, "bad which %d", which);
+  }
+  if (groups == 0) return MOE_OK;
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "src / dst is NULL");
+  if (src == dst) return fail(MOE_ERR_INVALID_ARG, "the layout change cannot run in place");
+  // check_cfg has d % 256 == 0 and f % 128 == 0: gate/up tiles of 128 + 128 rows, down tiles of 256 rows,
+  // 128-byte K stages
+  return hip_status(launch_pack_weights(src, dst, groups, rows, cols * esz, gateup, stream), "weight layout launch");
+}
+
 moe_status moe_transpose_fp8_weights(const uint8_t* q, const float* scales, int32_t batch, int32_t rows, int32_t cols,
                                      uint8_t* qt, float* scales_t, hipStream_t stream) {
   if (batch < 0 || rows <= 0 || cols <= 0) return fail(MOE_ERR_INVALID_ARG, "bad sizes batch=%d rows=%d cols=%d", batch, rows, cols);
@@ -720,6 +747,8 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
   MOE_TRY(check_bwd_cfg(cfg));
   MOE_TRY(check_layer_experts(cfg, layer));
   MOE_TRY(check_layer_experts(cfg, layer_t));
+  if (layer_t->weight_layout != MOE_LAYOUT_ROWS)
+    return fail(MOE_ERR_UNSUPPORTED, "layer_t (the transposed weights) must be in the row layout");
   const moe_config* c = cfg;
   const bool sh = c->n_shared > 0;
   const bool want_dx = dx_routed != nullptr, want_dw = dw13 != nullptr;
@@ -785,7 +814,9 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
   g.xs_routed = g.xs_shared = F(L.us);
   g.out_routed = base + L.gv_r;
   g.out_shared = base + L.gv_s;
+  g.packed = layer->weight_layout == MOE_LAYOUT_TILED;
   MOE_TRY(hip_status(launch_gemm_mfma(g, true, true, grid, s, true), "g/v GEMM launch"));
+  g.packed = 0;   // the transposed weights below are row-major
   // 2. dy quantized 1x128 along d; da = dy W2 (weights W2^T [f, d]: output f, contraction d), fp32
   MOE_TRY(hip_status(launch_quant_act(dy_routed, true, rows, d, base + L.dyq_r, F(L.dys_r), s), "dy quantization launch"));
   if (sh) MOE_TRY(hip_status(launch_quant_act(dy_shared, true, T, d, base + L.dyq_s, F(L.dys_s), s), "dy quantization launch"));

@@ -14,7 +14,8 @@
 // tokens go straight from global memory into registers in the MFMA operand layout (lane: row lane % 16,
 // 16-byte chunks g and 4 + g of the 128-byte K block, g = lane / 16), with kDecP K blocks in flight per
 // wave; all loads are plain vector loads, so the compiler's wait counts stay exact. The token rows are
-// the same for the 8 waves of a block and come from the vector L1 after the first wave.
+// the same for the 8 waves of a block and come from the vector L1 after the first wave. Weights in the
+// tiled layout (pack_weights in gemm_mfma.hip) are read as 1 KB contiguous per load instruction.
 #include "common.h"
 #include "kernels.h"
 
@@ -44,7 +45,7 @@ __device__ __forceinline__ i32x8 load_k_block(const uint8_t* row_k, int g) {
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-template <bool GATEUP, int kDecJ, int kDecP>
+template <bool GATEUP, int kDecJ, int kDecP, bool PACKED>
 __global__ __launch_bounds__(kDecThreads) void grouped_gemm_decode(GemmArgs a) {
   using Stage = DecStage<GATEUP, kDecJ>;
   constexpr int NA = Stage::NA;
@@ -81,12 +82,19 @@ __global__ __launch_bounds__(kDecThreads) void grouped_gemm_decode(GemmArgs a) {
   }
   uint32_t woff[NA];
   int wbrow[NA];                                   // weight block row of each operand
-  woff[0] = (uint32_t)(c0 + 16 * wave + tr) * K;
-  wbrow[0] = nt;
-  if constexpr (GATEUP) {
-    woff[1] = (uint32_t)(fg + c0 + 16 * wave + tr) * K;
-    wbrow[1] = fg / 128 + nt;
+  if constexpr (PACKED) {
+    // tiled layout: the 16-row block of this wave in stage 0 of its 256-row tile (gate/up: tile nt, gate
+    // block wave, up block 8 + wave; down: tile nt / 2, block 8 (nt % 2) + wave), lane-contiguous
+    const int tile = GATEUP ? nt : nt >> 1;
+    const int blk = GATEUP ? wave : 8 * (nt & 1) + wave;
+    woff[0] = ((uint32_t)tile * nkb << 15) + blk * 2048 + lane * 16;
+    if constexpr (GATEUP) woff[1] = woff[0] + 8 * 2048;
+  } else {
+    woff[0] = (uint32_t)(c0 + 16 * wave + tr) * K;
+    if constexpr (GATEUP) woff[1] = (uint32_t)(fg + c0 + 16 * wave + tr) * K;
   }
+  wbrow[0] = nt;
+  if constexpr (GATEUP) wbrow[1] = fg / 128 + nt;
 
   const uint8_t* X = shared ? a.x_shared : a.x_routed;
   const float* XS = shared ? a.xs_shared : a.xs_routed;
@@ -104,7 +112,14 @@ __global__ __launch_bounds__(kDecThreads) void grouped_gemm_decode(GemmArgs a) {
   auto load = [&](Stage& s, int kb) {
 #pragma unroll
     for (int t = 0; t < NA; ++t) {
-      s.a[t] = load_k_block(W + woff[t] + (size_t)kb * 128, g);
+      if constexpr (PACKED) {
+        const uint8_t* p = W + woff[t] + ((size_t)kb << 15);
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 1024);
+        s.a[t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        s.a[t] = load_k_block(W + woff[t] + (size_t)kb * 128, g);
+      }
       s.ws[t] = WS[(size_t)wbrow[t] * nkb + kb];
     }
 #pragma unroll
@@ -212,8 +227,13 @@ hipError_t launch_gemm_decode(const GemmArgs& a, bool gateup, hipStream_t s) {
   const int nt_s = a.fs > 0 ? (gateup ? a.fs / 128 : a.d / 128) : 0;
   const int blocks = a.E * nt_r + nt_s;
   if (blocks == 0) return hipSuccess;
-  if (gateup) grouped_gemm_decode<true, kDecJG, kDecPG><<<blocks, kDecThreads, 0, s>>>(a);
-  else grouped_gemm_decode<false, kDecJD, kDecPD><<<blocks, kDecThreads, 0, s>>>(a);
+  if (a.packed) {
+    if (gateup) grouped_gemm_decode<true, kDecJG, kDecPG, true><<<blocks, kDecThreads, 0, s>>>(a);
+    else grouped_gemm_decode<false, kDecJD, kDecPD, true><<<blocks, kDecThreads, 0, s>>>(a);
+  } else {
+    if (gateup) grouped_gemm_decode<true, kDecJG, kDecPG, false><<<blocks, kDecThreads, 0, s>>>(a);
+    else grouped_gemm_decode<false, kDecJD, kDecPD, false><<<blocks, kDecThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -26,6 +26,8 @@
 // registers. Waves whose 128 tokens all lie past the tile's last row skip the multiply.
 // The grid is persistent: blocks are split by XCD (block id mod 8) and each XCD walks one contiguous
 // range of the tile list, in which neighbouring tiles share an expert's weight tile in that XCD's L2.
+// Weights come either row-major or in the tiled layout of pack_weights below, where every 32 KB weight
+// stage of a tile is contiguous in HBM and already in the MFMA operand order.
 #include "common.h"
 #include "kernels.h"
 
@@ -101,7 +103,7 @@ __device__ __forceinline__ TileInfo decode_tile_lds(int id, const int32_t* mtp, 
 // One K stage of one wave: its four 16-row weight tiles against its eight 16-token tiles. E4M3: every
 // 16x16x128 product is a fresh partial sum, scaled by (token scale x weight block scale) and added into
 // fp32 one MFMA after it is issued, so the matrix core and the vector ALU overlap.
-template <bool FP8, bool GATEUP>
+template <bool FP8, bool GATEUP, bool PACKED>
 __device__ __forceinline__ void mma_stage(f32x4 (&acc)[4][kTJ], const uint8_t* __restrict__ slot, int wn, int tok0,
                                           int tr, int g) {
   const uint8_t* A = slot;
@@ -111,12 +113,19 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[4][kTJ], const uint8_t* _
     hi = *reinterpret_cast<const i32x4*>(base + row * kStageB + (((4 + g) ^ (row & 7)) * 16));
   };
   // weight rows of tile i: gate/up -> gate rows 32 wn + 16 i (i < 2) and the matching up rows 128 + ...;
-  // down -> rows 64 wn + 16 i
+  // down -> rows 64 wn + 16 i. In the tiled layout those are 16-row blocks 2 wn + i (+ 8 for up) or
+  // 4 wn + i of the stage, each 2 KB in operand order: lane l's chunks g and 4 + g at 16 l and 1024 + 16 l.
   i32x4 a[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = (GATEUP ? (i < 2 ? 0 : 128) + 32 * wn + 16 * (i & 1) : 64 * wn + 16 * i) + tr;
-    rd(A, row, a[i][0], a[i][1]);
+    const int blk = GATEUP ? (i < 2 ? 0 : 8) + 2 * wn + (i & 1) : 4 * wn + i;
+    if constexpr (PACKED) {
+      const uint8_t* p = A + blk * 2048 + (16 * g + tr) * 16;
+      a[i][0] = *reinterpret_cast<const i32x4*>(p);
+      a[i][1] = *reinterpret_cast<const i32x4*>(p + 1024);
+    } else {
+      rd(A, 16 * blk + tr, a[i][0], a[i][1]);
+    }
   }
   i32x4 b[2][2];
   rd(B, tok0 + tr, b[0][0], b[0][1]);
@@ -177,7 +186,7 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[4][kTJ], const uint8_t* _
 
 // RAW: the accumulators are stored in fp32 as they are (gate/up: g and v, no SwiGLU; down: fp32 instead
 // of bf16), for the input backward of the experts.
-template <bool FP8, bool GATEUP, bool RAW = false>
+template <bool FP8, bool GATEUP, bool RAW, bool PACKED>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -314,14 +323,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
     }
     const int kk = live ? kl : 0;
     ++kl;
-    // weight rows: LDS row 64 q + lrow is W1 row c0 + 64 q + lrow (q < 2) or W3 row fg + c0 + 64 q - 128 +
-    // lrow (gate/up, c0 = 128 n_tile); W2 row c0 + 64 q + lrow (down, c0 = 256 n_tile)
-    const int c0 = tl.n_tile * (GATEUP ? 128 : kBW);
-    const uint8_t* Wk = Wl + (size_t)kk * kStageB + lchunk;
+    if constexpr (PACKED) {
+      // the stage's 32 KB are contiguous and land in LDS as they are
+      const uint8_t* Wk = Wl + ((size_t)(tl.n_tile * nst_l + kk) << 15) + tid * 16;
 #pragma unroll
-    for (int q = 0; q < kChunks; ++q) {
-      const int wrow = (GATEUP && q >= 2) ? fg_l + c0 + 64 * q - 128 : c0 + 64 * q;
-      dma16(Wk + (size_t)(wrow + lrow) * kbytes_l, sl + (q * kThreads + wave * 64) * 16);
+      for (int q = 0; q < kChunks; ++q) dma16(Wk + q * kThreads * 16, sl + (q * kThreads + wave * 64) * 16);
+    } else {
+      // weight rows: LDS row 64 q + lrow is W1 row c0 + 64 q + lrow (q < 2) or W3 row fg + c0 + 64 q - 128 +
+      // lrow (gate/up, c0 = 128 n_tile); W2 row c0 + 64 q + lrow (down, c0 = 256 n_tile)
+      const int c0 = tl.n_tile * (GATEUP ? 128 : kBW);
+      const uint8_t* Wk = Wl + (size_t)kk * kStageB + lchunk;
+#pragma unroll
+      for (int q = 0; q < kChunks; ++q) {
+        const int wrow = (GATEUP && q >= 2) ? fg_l + c0 + 64 * q - 128 : c0 + 64 * q;
+        dma16(Wk + (size_t)(wrow + lrow) * kbytes_l, sl + (q * kThreads + wave * 64) * 16);
+      }
     }
     const uint8_t* Xk = Xl + (size_t)kk * kStageB;
     // 64-row groups of the token tile past its last row are not copied: their LDS rows keep older data,
@@ -349,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
     wait_vm0();       // this wave's copies of stage gs have landed
     barrier_lds();    // ... and every wave's; every wave is done with the other slot
     issue(lds + ((gs + 1) & 1) * kSlot);
-    if (tok0 < tc.nrows) mma_stage<FP8, GATEUP>(acc, cur, wn, tok0, tr, g);
+    if (tok0 < tc.nrows) mma_stage<FP8, GATEUP, PACKED>(acc, cur, wn, tok0, tr, g);
     if (++kb < nst_c) continue;
 
     // ---- epilogue of tile tc. Lane holds, for token tok0 + 16 j + tr, channels 4 g + r of each 16-row
@@ -470,26 +486,62 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
 
 int gemm_mfma_bm() { return kBM; }
 
+template <bool FP8, bool GATEUP, bool RAW, bool PACKED>
+hipError_t launch_variant(const GemmArgs& a, int grid, hipStream_t s) {
+  static std::atomic<bool> attr_done{false};   // set once per kernel (setting it twice is harmless)
+  const void* fn = (const void*)grouped_gemm_mfma<FP8, GATEUP, RAW, PACKED>;
+  if (!attr_done.load(std::memory_order_relaxed)) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_done.store(true, std::memory_order_relaxed);
+  }
+  grouped_gemm_mfma<FP8, GATEUP, RAW, PACKED><<<grid, kThreads, kLdsBytes, s>>>(a);
+  return hipGetLastError();
+}
+
+template <bool PACKED>
+hipError_t launch_layout(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s, bool raw) {
+  if (raw) return gateup ? launch_variant<true, true, true, PACKED>(a, grid, s) : launch_variant<true, false, true, PACKED>(a, grid, s);
+  if (fp8) return gateup ? launch_variant<true, true, false, PACKED>(a, grid, s) : launch_variant<true, false, false, PACKED>(a, grid, s);
+  return gateup ? launch_variant<false, true, false, PACKED>(a, grid, s) : launch_variant<false, false, false, PACKED>(a, grid, s);
+}
+
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s, bool raw) {
   if (raw && !fp8) return hipErrorInvalidValue;
-  static std::atomic<bool> attr_done[6];   // set once per kernel (setting it twice is harmless)
-  const int k = raw ? 4 + (gateup ? 1 : 0) : (fp8 ? 2 : 0) + (gateup ? 1 : 0);
-  const void* fns[6] = {(const void*)grouped_gemm_mfma<false, false>, (const void*)grouped_gemm_mfma<false, true>,
-                        (const void*)grouped_gemm_mfma<true, false>, (const void*)grouped_gemm_mfma<true, true>,
-                        (const void*)grouped_gemm_mfma<true, false, true>, (const void*)grouped_gemm_mfma<true, true, true>};
-  if (!attr_done[k].load(std::memory_order_relaxed)) {
-    hipError_t e = hipFuncSetAttribute(fns[k], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_done[k].store(true, std::memory_order_relaxed);
+  return a.packed ? launch_layout<true>(a, fp8, gateup, grid, s, raw) : launch_layout<false>(a, fp8, gateup, grid, s, raw);
+}
+
+// ---- the tiled weight layout. For each group (a routed expert, or the shared block), each N tile of 256
+// weight rows (gate/up: W1 rows 128 n .. 128 n + 127 then the W3 rows f + 128 n ..; down: rows 256 n ..)
+// and each 128-byte K stage k, 32 KB at ((n * stages + k) << 15): the tile's sixteen 16-row blocks, 2 KB
+// each, and in a block the 16-byte chunk c (of 8) of row r (of 16) at byte 16 (64 (c / 4) + 16 (c % 4) + r),
+// i.e. lane 16 (c % 4) + r of the MFMA operand, low half for c < 4, high half after 1 KB. One thread per
+// 16-byte chunk of the output.
+__global__ void pack_weights(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int rows, int row_bytes,
+                             int gateup, long long per_group, long long total) {
+  const int stages = row_bytes / kStageB;
+  for (long long c = blockIdx.x * (long long)blockDim.x + threadIdx.x; c < total; c += (long long)gridDim.x * blockDim.x) {
+    const long long grp = c / per_group;
+    const long long r = c - grp * per_group;
+    const int lane = (int)(r & 63), half = (int)((r >> 6) & 1), blk = (int)((r >> 7) & 15);
+    const long long nk = r >> 11;
+    const int n = (int)(nk / stages), k = (int)(nk - (long long)n * stages);
+    const int row = (gateup ? (blk < 8 ? 128 * n + 16 * blk : rows / 2 + 128 * n + 16 * (blk - 8)) : 256 * n + 16 * blk) +
+                    (lane & 15);
+    const size_t so = (size_t)grp * rows * row_bytes + (size_t)row * row_bytes + (size_t)k * kStageB +
+                      (4 * half + (lane >> 4)) * 16;
+    *reinterpret_cast<i32x4*>(dst + c * 16) = *reinterpret_cast<const i32x4*>(src + so);
   }
-  switch (k) {
-    case 0: grouped_gemm_mfma<false, false><<<grid, kThreads, kLdsBytes, s>>>(a); break;
-    case 1: grouped_gemm_mfma<false, true><<<grid, kThreads, kLdsBytes, s>>>(a); break;
-    case 2: grouped_gemm_mfma<true, false><<<grid, kThreads, kLdsBytes, s>>>(a); break;
-    case 3: grouped_gemm_mfma<true, true><<<grid, kThreads, kLdsBytes, s>>>(a); break;
-    case 4: grouped_gemm_mfma<true, false, true><<<grid, kThreads, kLdsBytes, s>>>(a); break;
-    default: grouped_gemm_mfma<true, true, true><<<grid, kThreads, kLdsBytes, s>>>(a); break;
-  }
+}
+
+hipError_t launch_pack_weights(const void* src, void* dst, int groups, int rows, int row_bytes, bool gateup,
+                               hipStream_t s) {
+  const long long per_group = (long long)rows * row_bytes / 16;
+  const long long total = per_group * groups;
+  if (total == 0) return hipSuccess;
+  const int blocks = (int)std::min<long long>((total + 255) / 256, 65536);
+  pack_weights<<<blocks, 256, 0, s>>>(static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), rows, row_bytes,
+                                      gateup ? 1 : 0, per_group, total);
   return hipGetLastError();
 }
 

@@ -105,6 +105,7 @@ struct GemmArgs {
   uint8_t* out_shared;
   float* out_scale_routed;    // gate/up fp8: scales of a
   float* out_scale_shared;
+  int packed;                 // weights in the tiled layout of launch_pack_weights (matrix-core kernels only)
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
@@ -126,6 +127,11 @@ hipError_t launch_schedule_mfma(const int32_t* offsets, int E, int T, int bm, co
 int gemm_mfma_bm();
 // raw (E4M3 only): fp32 accumulators out (gate/up: g and v without SwiGLU; down: fp32 instead of bf16)
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s, bool raw = false);
+// weights of `groups` groups of [rows, row_bytes] (row-major, one group after the other) -> the tiled
+// layout the matrix-core and decode kernels read with GemmArgs::packed (gateup: rows = 2 x inner dim,
+// W1 rows then W3 rows; else W2 rows); rows % 256 == 0, row_bytes % 128 == 0
+hipError_t launch_pack_weights(const void* src, void* dst, int groups, int rows, int row_bytes, bool gateup,
+                               hipStream_t s);
 hipError_t launch_swiglu_backward_quant(const float* da, const float* gv, int rows, int fg, uint8_t* q, float* scales,
                                         hipStream_t s);
 hipError_t launch_transpose_fp8(const uint8_t* q, const float* scales, int batch, int rows, int cols, uint8_t* qt,

@@ -12,8 +12,9 @@ import torch
 
 from synth import configs, device as sdev
 
-from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_GATE_SIGMOID_BIAS, MOE_GATE_SOFTMAX, make_config, make_layer,
-               moe_quantize_weights)
+from . import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_GATE_SIGMOID_BIAS, MOE_GATE_SOFTMAX, MOE_LAYOUT_ROWS,
+               MOE_LAYOUT_TILED, MOE_PACK_W13, MOE_PACK_W2, MOE_PACK_WS13, MOE_PACK_WS2, make_config, make_layer,
+               moe_pack_weights, moe_quantize_weights)
 
 
 @dataclasses.dataclass
@@ -21,7 +22,7 @@ class DeviceLayer:
     w: configs.Workload
     cfg: object
     layer: object
-    t: dict     # device tensors kept alive for `layer`
+    t: dict     # device tensors kept alive for `layer`; w13, w2, ws13, ws2 always in the row layout
 
 
 def workload_config(w: configs.Workload):
@@ -42,7 +43,22 @@ def _fill_w2(dst, w, e):
     sdev.fill_normal(dst, w.seed, configs.STREAM_SH_W2 if e < 0 else configs.stream_routed(e, 2), configs.sigma_down(w))
 
 
-def device_layer(w: configs.Workload, device: str = "cuda", chunk: int = 16) -> DeviceLayer:
+def _tiled(cfg, t, layer_args):
+    """Copies of the expert weights in the tiled layout (the form the expert GEMMs stream fastest); the
+    row-layout tensors stay in t for callers that need them (the backward's transposed weights)."""
+    for key, which in (("w13", MOE_PACK_W13), ("w2", MOE_PACK_W2), ("ws13", MOE_PACK_WS13), ("ws2", MOE_PACK_WS2)):
+        if key in t:
+            t[key + "_tiled"] = torch.empty_like(t[key])
+            moe_pack_weights(cfg, which, t[key], t[key + "_tiled"])
+    for key in ("w13", "w2", "ws13", "ws2"):
+        if key in t:
+            layer_args[key] = t[key + "_tiled"]
+    layer_args["weight_layout"] = MOE_LAYOUT_TILED
+
+
+def device_layer(w: configs.Workload, device: str = "cuda", chunk: int = 16, tiled: bool = True) -> DeviceLayer:
+    """The workload's layer on the device. tiled: bf16 / fp8 expert weights in the tiled layout (the
+    layer struct points at those copies); fp32 weights are always row-major."""
     t = {}
     adt = torch.float32 if w.act == "f32" else torch.bfloat16
     t["u"] = sdev.fill_normal(torch.empty((w.T, w.d), dtype=adt, device=device), w.seed, configs.STREAM_U, 1.0)
@@ -62,7 +78,11 @@ def device_layer(w: configs.Workload, device: str = "cuda", chunk: int = 16) -> 
             t["ws2"] = torch.empty((w.d, w.fs), dtype=wdt, device=device)
             _fill_w13(t["ws13"], w, -1, w.fs)
             _fill_w2(t["ws2"], w, -1)
-        layer = make_layer(t["w13"], t["w2"], t["wg"], ws13=t.get("ws13"), ws2=t.get("ws2"), logit_offset=t["off"])
+        args = dict(w13=t["w13"], w2=t["w2"], w_gate=t["wg"], ws13=t.get("ws13"), ws2=t.get("ws2"),
+                    logit_offset=t["off"], weight_layout=MOE_LAYOUT_ROWS)
+        if tiled and w.wdt == "bf16":
+            _tiled(workload_config(w), t, args)
+        layer = make_layer(**args)
     else:
         t["w13"] = torch.empty((w.E, 2 * w.f, w.d), dtype=torch.uint8, device=device)
         t["w13s"] = torch.empty((w.E, 2 * w.f // 128, w.d // 128), dtype=torch.float32, device=device)
@@ -90,8 +110,11 @@ def device_layer(w: configs.Workload, device: str = "cuda", chunk: int = 16) -> 
             moe_quantize_weights(s13, t["ws13"], t["ws13s"])
             moe_quantize_weights(s2, t["ws2"], t["ws2s"])
             del s13, s2
-        layer = make_layer(t["w13"], t["w2"], t["wg"], ws13=t.get("ws13"), ws2=t.get("ws2"), w13_scale=t["w13s"],
-                           w2_scale=t["w2s"], ws13_scale=t.get("ws13s"), ws2_scale=t.get("ws2s"),
-                           logit_offset=t["off"])
+        args = dict(w13=t["w13"], w2=t["w2"], w_gate=t["wg"], ws13=t.get("ws13"), ws2=t.get("ws2"),
+                    w13_scale=t["w13s"], w2_scale=t["w2s"], ws13_scale=t.get("ws13s"), ws2_scale=t.get("ws2s"),
+                    logit_offset=t["off"], weight_layout=MOE_LAYOUT_ROWS)
+        if tiled:
+            _tiled(workload_config(w), t, args)
+        layer = make_layer(**args)
     torch.cuda.synchronize()
     return DeviceLayer(w, workload_config(w), layer, t)

@@ -54,6 +54,15 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
  * sigmoid affinity with the selection-only bias (same report, 3.3). */
 typedef enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID_BIAS = 1 } moe_gate;
 
+/* Storage of the expert weight matrices of a layer (moe_layer.weight_layout). */
+typedef enum {
+  MOE_LAYOUT_ROWS = 0,   /* row-major, as documented at moe_layer */
+  MOE_LAYOUT_TILED = 1   /* the tiled layout written by moe_pack_weights (bf16 and fp8 weights) */
+} moe_weight_layout;
+
+/* Which weight matrix moe_pack_weights converts. */
+typedef enum { MOE_PACK_W13 = 0, MOE_PACK_W2 = 1, MOE_PACK_WS13 = 2, MOE_PACK_WS2 = 3 } moe_pack_which;
+
 typedef struct {
   int32_t T;           /* tokens (>= 0; T == 0 is a no-op) */
   int32_t d_model;     /* d */
@@ -83,7 +92,11 @@ typedef struct {
  *  ws13 [2fs, d], ws2 [d, fs] (+ ws13_scale [2fs/128, d/128], ws2_scale [d/128, fs/128]): the shared
  *             experts as one block; NULL when Ks == 0.
  *  w_gate     [E, d] fp32: the expert centroids e_i of the gate (logit z_{t,i} = u_t . e_i).
- *  logit_offset [E] fp32 or NULL: added to every logit before gating (a fixed per-expert skew). */
+ *  logit_offset [E] fp32 or NULL: added to every logit before gating (a fixed per-expert skew).
+ *  weight_layout  moe_weight_layout of w13, w2, ws13 and ws2 (all four alike; the scales keep their
+ *             layout). MOE_LAYOUT_TILED holds the same values as the row layout, reordered by
+ *             moe_pack_weights so that the expert GEMMs read every weight stage as one contiguous run;
+ *             results are bit-identical. Zero (a zero-initialised struct) is the row layout. */
 typedef struct {
   const void* w13;
   const void* w2;
@@ -95,6 +108,7 @@ typedef struct {
   const float* ws2_scale;
   const float* w_gate;
   const float* logit_offset;
+  int32_t weight_layout;
 } moe_layer;
 
 /* Bytes of workspace every call below needs for this configuration (host output). */
@@ -208,10 +222,11 @@ moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float g
  *   dx    = [dg | dv] [W1; W3], with [dg | dv] quantized 1x128 along 2f.
  *  cfg      E4M3 experts (w_dtype MOE_FP8_E4M3), n_shared 0 or 1, inter_dim % 256 == 0 and
  *           2 * inter_dim <= 8192 (else MOE_ERR_UNSUPPORTED).
- *  layer    the forward weights (w13, w13_scale, ws13, ws13_scale are used).
- *  layer_t  the same weights transposed (moe_transpose_fp8_weights): w13 = [W1; W3]^T [E, d, 2f] with
- *           scales [E, d/128, 2f/128], w2 = W2^T [E, f, d] with scales [E, f/128, d/128]; ws13 / ws2
- *           likewise for the shared block.
+ *  layer    the forward weights (w13, w13_scale, ws13, ws13_scale are used), in either layout.
+ *  layer_t  the same weights transposed (moe_transpose_fp8_weights, from the row layout): w13 =
+ *           [W1; W3]^T [E, d, 2f] with scales [E, d/128, 2f/128], w2 = W2^T [E, f, d] with scales
+ *           [E, f/128, d/128]; ws13 / ws2 likewise for the shared block. Row layout only
+ *           (MOE_ERR_UNSUPPORTED otherwise).
  *  u [T, d] bf16 (the layer input), offsets / perm_src as moe_dispatch returns them.
  *  dy_routed [T*K, d] bf16, dy_shared [T, d] bf16 (n_shared == 1); dx_routed [T*K, d] bf16 out,
  *  dx_shared [T, d] bf16 out.
@@ -244,6 +259,22 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
                                    const void* u, const int32_t* offsets, const int32_t* perm_src, const void* dy_routed,
                                    const void* dy_shared, void* dx_routed, void* dx_shared, void* dw13, void* dw2,
                                    void* dws13, void* dws2, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert weights in the row layout -> MOE_LAYOUT_TILED (a reordering of bytes: the expert GEMMs then read
+ * each 128-byte K stage of a tile of 256 weight rows as 32 contiguous KB, in the order the matrix cores
+ * take their operands; the values and every result are unchanged). For each expert (or the shared block)
+ * and each tile n of 256 rows (W13: W1 rows 128 n .. 128 n + 127, then the W3 rows f + 128 n ..; W2: rows
+ * 256 n ..) and K stage k (128 bytes of a row: 128 E4M3 or 64 bf16 values), 32 KB at offset
+ * (n * stages + k) * 32768 of that expert's matrix: sixteen 2 KB blocks of 16 rows, and in block b the
+ * 16-byte chunk c (0..7) of the block's row r (0..15) at byte 16 * (64 * (c / 4) + 16 * (c % 4) + r).
+ * Scales are not touched.
+ *  cfg    bf16 or fp8 weights (the sizes come from it; its T is not used).
+ *  which  MOE_PACK_W13 (src/dst [E, 2f, d]), MOE_PACK_W2 ([E, d, f]), MOE_PACK_WS13 ([2 Ks f, d]),
+ *         MOE_PACK_WS2 ([d, Ks f]); the shared ones are a no-op when Ks == 0.
+ *  src, dst  device buffers of the matrix's size, caller-owned, not overlapping (MOE_ERR_INVALID_ARG
+ *         when src == dst).
+ * Asynchronous on `stream`. */
+moe_status moe_pack_weights(const moe_config* cfg, int32_t which, const void* src, void* dst, hipStream_t stream);
 
 /* Transpose a batch of E4M3 matrices with their 128x128 block scales: qt[m] = q[m]^T ([cols, rows]),
  * scales_t[m] = scales[m]^T ([cols/128, rows/128]); the codes are unchanged, so a transposed block keeps

@@ -185,3 +185,22 @@ def test_noalloc_forward_rejects_oversized_configs_before_any_launch():
     st = lib.moe_forward_noalloc(ctypes.byref(cfg), ctypes.byref(lay), None, None, None, None, None, None)
     assert st == moe.MOE_ERR_WORKSPACE
     assert "scratch" in moe.moe_last_error()
+
+
+def test_weight_layout_argument_errors():
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    lib.moe_pack_weights.argtypes = [ctypes.POINTER(moe.moe_config), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    cfg = _cfg()
+    f32 = _cfg(act_dtype=moe.MOE_F32, w_dtype=moe.MOE_F32)
+    assert lib.moe_pack_weights(ctypes.byref(f32), moe.MOE_PACK_W13, 16, 32, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_pack_weights(ctypes.byref(cfg), 4, 16, 32, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_pack_weights(ctypes.byref(cfg), moe.MOE_PACK_W2, 16, 16, None) == moe.MOE_ERR_INVALID_ARG  # in place
+    assert lib.moe_pack_weights(ctypes.byref(cfg), moe.MOE_PACK_W2, None, 16, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_pack_weights(ctypes.byref(_cfg(n_shared=0)), moe.MOE_PACK_WS13, None, None, None) == moe.MOE_OK
+    # a layer in an unknown layout, or fp32 weights in the tiled one, is refused before any launch
+    lib.moe_expert_ffn.argtypes = [ctypes.POINTER(moe.moe_config), ctypes.POINTER(moe.moe_layer)] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]
+    bad = moe.moe_layer(16, 16, 16, 16, 16, 16, 16, 16, 16, None, 2)
+    assert lib.moe_expert_ffn(ctypes.byref(cfg), ctypes.byref(bad), 16, 16, 16, 16, 16, 16, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    tiled32 = moe.moe_layer(16, 16, None, None, 16, 16, None, None, 16, None, moe.MOE_LAYOUT_TILED)
+    assert lib.moe_expert_ffn(ctypes.byref(f32), ctypes.byref(tiled32), 16, 16, 16, 16, 16, 16, 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
