@@ -105,7 +105,7 @@ moe_status check_cfg(const moe_config* c) {
 }
 
 struct Layout {
-  size_t z, z64, wg_split, zpart, recheck_count, recheck_list, wn2;
+  size_t z, z64, wg_split, zpart, recheck_count, recheck_list, wn2, un2;
   size_t chunk_counts, chunk_base, mt_prefix, xsched;
   size_t uq, us, a_r, a_s, as_r, as_s;
   size_t f_idx, f_w, f_counts, f_offsets, f_perm, f_rowof, f_yr, f_ys;
@@ -135,6 +135,7 @@ Layout layout(const moe_config* c) {
   L.recheck_count = take(16);
   L.recheck_list = take(T * 4);
   L.wn2 = take(E * 4);
+  L.un2 = take(use_mfma_router(c) ? 4 * T * 4 : 0);
   const size_t nch = dispatch_chunks(c->T);
   L.chunk_counts = take(nch * E * 4);
   L.chunk_base = take(nch * E * 4);
@@ -356,6 +357,7 @@ RouteArgs route_args(const moe_config* c, const moe_layer* l, const void* u, con
   a.topk_groups = c->topk_groups;
   a.delta = c->gate == MOE_GATE_SOFTMAX ? kRecheckDeltaSoftmax : kRecheckDeltaSigmoid;
   a.wn2 = reinterpret_cast<float*>(base + L.wn2);
+  a.un2 = reinterpret_cast<float*>(base + L.un2);
   a.z = reinterpret_cast<float*>(base + L.z);
   a.z64 = reinterpret_cast<double*>(base + L.z64);
   a.wg_split = reinterpret_cast<uint16_t*>(base + L.wg_split);

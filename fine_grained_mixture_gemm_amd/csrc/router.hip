@@ -88,18 +88,35 @@ __global__ __launch_bounds__(256) void router_logits_sum(const double* __restric
 // w_gate is split exactly into three bf16 parts, w = hi + mid + lo (hi and mid truncate, lo holds the
 // last 8 significant bits); bf16 x bf16 products are exact in fp32, so the three bf16 GEMMs
 // accumulated in fp32 give the fp32 product of the bf16 tokens with the fp32 centroids.
-__global__ __launch_bounds__(256) void router_split_wg(const float* __restrict__ wg, long long n,
-                                                       uint16_t* __restrict__ parts) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const float w = wg[i];
+__device__ __forceinline__ void split_bf16x3(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
   const uint32_t hb = __float_as_uint(w) & 0xFFFF0000u;
   const float r1 = w - __uint_as_float(hb);
   const uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
   const float r2 = r1 - __uint_as_float(mb);
-  parts[i] = (uint16_t)(hb >> 16);
-  parts[n + i] = (uint16_t)(mb >> 16);
-  parts[2 * n + i] = f32_to_bf16(r2);
+  hi = (uint16_t)(hb >> 16);
+  mid = (uint16_t)(mb >> 16);
+  lo = f32_to_bf16(r2);
+}
+
+// One block per routed expert: wn2[e] = |e_e|^2 (for the recheck margin) and, with SPLIT, the three bf16
+// parts of the centroid row for the MFMA logits (parts [3][E][d]).
+template <bool SPLIT>
+__global__ __launch_bounds__(256) void router_prep_wg(const float* __restrict__ wg, int E, int d,
+                                                      float* __restrict__ wn2, uint16_t* __restrict__ parts) {
+  __shared__ float part[4];
+  const int e = blockIdx.x;
+  const size_t n = (size_t)E * d;
+  float s = 0.f;
+  for (int k = threadIdx.x; k < d; k += 256) {
+    const size_t i = (size_t)e * d + k;
+    const float v = wg[i];
+    s = fmaf(v, v, s);
+    if constexpr (SPLIT) split_bf16x3(v, parts[i], parts[n + i], parts[2 * n + i]);
+  }
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) wn2[e] = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // 128 tokens x 64 experts per block; wave w owns experts 16w..16w+15 against all 128 tokens.
@@ -107,10 +124,12 @@ __global__ __launch_bounds__(256) void router_split_wg(const float* __restrict__
 // the centroid parts stream from global memory into registers. blockIdx.z takes the slice
 // [z klen, (z + 1) klen) of d: with one slice the kernel writes z = sum + off, with several it writes
 // the slice's fp32 partial sum to zpart[z] and router_logits_sum32 adds the slices in order.
+// Blocks of the first 64 experts also add up the squares of their token rows over their slice of d
+// (un2part[slice][t], for the recheck margin; nullptr: not wanted).
 __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ u, const uint16_t* __restrict__ parts,
                                                           const float* __restrict__ off, int T, int E, int d,
                                                           int klen, float* __restrict__ z, float* __restrict__ zpart,
-                                                          int* __restrict__ recheck_count) {
+                                                          int* __restrict__ recheck_count, float* __restrict__ un2part) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][128 * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * 128, e0 = blockIdx.y * 64;
@@ -141,12 +160,21 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
     A[p][1] = *reinterpret_cast<const i32x4*>(wp + p * n * 2 + 64);
   }
   const int tr = lane & 15, g = lane >> 4;
+  const bool norms = un2part != nullptr && blockIdx.y == 0;
+  float su[4] = {0.f, 0.f, 0.f, 0.f};      // squares of this thread's 8-element pieces of rows 32 q + tid / 8
   for (int kb = 0; kb < nst; ++kb) {
     uint8_t* buf = lds[kb & 1];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int id16 = q * 256 + tid, row = id16 >> 3, c = id16 & 7;
       *reinterpret_cast<i32x4*>(buf + row * 128 + ((c ^ (row & 7)) * 16)) = Bst[q];
+      if (norms) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = __uint_as_float((uint32_t)Bst[q][i] << 16), hi = __uint_as_float((uint32_t)Bst[q][i] & 0xFFFF0000u);
+          su[q] = fmaf(hi, hi, fmaf(lo, lo, su[q]));
+        }
+      }
     }
     __syncthreads();
     if (kb + 1 < nst) {
@@ -183,6 +211,18 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
       }
     }
   }
+  if (norms) {
+    // the 8 threads tid & ~7 .. tid | 7 hold the pieces of one row
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v = su[q];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      const int t = t0 + 32 * q + (tid >> 3);
+      if ((tid & 7) == 0 && t < T) un2part[(size_t)blockIdx.z * T + t] = v;
+    }
+  }
   // lane holds experts 16 wave + 4 (lane >> 4) + r for token 16 j + (lane & 15)
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -210,8 +250,7 @@ __global__ __launch_bounds__(256) void router_logits_sum32(const float* __restri
 }
 
 void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s) {
-  const long long n = (long long)a.E * a.d;
-  router_split_wg<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.wg, n, a.wg_split);
+  router_prep_wg<true><<<a.E, 256, 0, s>>>(a.wg, a.E, a.d, a.wn2, a.wg_split);
   // several slices of d when one gives fewer than two blocks per CU; their fp32 partial sums live in the
   // space of the fp64 recheck logits (sized for four slices), which are written only later
   const int ks = router_mfma_slices(a.T, a.E, a.d);
@@ -219,7 +258,7 @@ void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s) {
   float* zp = ks > 1 ? reinterpret_cast<float*>(a.z64) : nullptr;
   dim3 grid(cdiv(a.T, 128), cdiv(a.E, 64), ks);
   router_logits_mfma<<<grid, 256, 0, s>>>((const uint16_t*)a.u, a.wg_split, a.off, a.T, a.E, a.d, klen, a.z, zp,
-                                          a.recheck_count);
+                                          a.recheck_count, a.un2);
   if (ks > 1) {
     const long long nz = (long long)a.T * a.E;
     const long long nb = (nz + 255) / 256;
@@ -231,34 +270,24 @@ void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s) {
 // The fp32 logits round every partial sum of u_t . e_i; each rounding is proportional to the running sum,
 // which is at most |u_t| |e_i| (Cauchy-Schwarz). The base margin holds for |u_t| |e_i| up to sqrt(d) (token
 // rows of RMS 1 against centroids of norm 1); a token whose |u_t| max_i |e_i| is larger gets the margin
-// scaled by the ratio. wn2[i] = |e_i|^2, one block per routed expert.
-__global__ __launch_bounds__(256) void router_centroid_norms(const float* __restrict__ wg, int E, int d,
-                                                             float* __restrict__ wn2) {
-  __shared__ float part[4];
-  const int e = blockIdx.x;
-  float s = 0.f;
-  for (int k = threadIdx.x; k < d; k += 256) {
-    const float v = wg[(size_t)e * d + k];
-    s = fmaf(v, v, s);
-  }
-  s = wave_sum(s);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) wn2[e] = (part[0] + part[1]) + (part[2] + part[3]);
-}
-
-// delta * max(1, |u_t| max_i |e_i| / sqrt(d)) for the token row u_t, on one wave
+// scaled by the ratio. wn2[i] = |e_i|^2 comes from router_prep_wg.
+// delta * max(1, |u_t| max_i |e_i| / sqrt(d)) for token t, on one wave. |u_t|^2 is the sum of the nsl
+// slice partials un2[s][t] the MFMA logits wrote, or (un2 == nullptr) is summed here from the row.
 template <typename TU>
-__device__ __forceinline__ float token_margin(const TU* __restrict__ ut, int d, const float* __restrict__ wn2, int E,
-                                              float delta, int lane) {
+__device__ __forceinline__ float token_margin(const TU* __restrict__ ut, int d, const float* __restrict__ un2, int nsl,
+                                              int t, int T, const float* __restrict__ wn2, int E, float delta, int lane) {
   float su = 0.f;
-  for (int k = lane; k < d; k += 64) {
-    float v;
-    if constexpr (sizeof(TU) == 2) v = bf16_to_f32(ut[k]);
-    else v = ut[k];
-    su = fmaf(v, v, su);
+  if (un2) {
+    for (int sl = 0; sl < nsl; ++sl) su += un2[(size_t)sl * T + t];
+  } else {
+    for (int k = lane; k < d; k += 64) {
+      float v;
+      if constexpr (sizeof(TU) == 2) v = bf16_to_f32(ut[k]);
+      else v = ut[k];
+      su = fmaf(v, v, su);
+    }
+    su = wave_sum(su);
   }
-  su = wave_sum(su);
   float wm = 0.f;
   for (int e = lane; e < E; e += 64) wm = fmaxf(wm, wn2[e]);
   wm = wave_max(wm);
@@ -357,7 +386,7 @@ template <int GATE, typename TU>
 __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, int T, int E, int K,
                                                    const float* __restrict__ bias, int renorm, int G, int M,
                                                    float delta, const TU* __restrict__ u, int d,
-                                                   const float* __restrict__ wn2,
+                                                   const float* __restrict__ un2, int nsl, const float* __restrict__ wn2,
                                                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                    int* __restrict__ recheck_count, int* __restrict__ recheck_list) {
   const int lane = threadIdx.x & 63;
@@ -424,7 +453,7 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, 
     topk_idx[(size_t)t * K + rank] = my_e;
     topk_w[(size_t)t * K + rank] = g;
   }
-  const float margin = token_margin(u + (size_t)t * d, d, wn2, E, delta, lane);
+  const float margin = token_margin(u + (size_t)t * d, d, un2, nsl, t, T, wn2, E, delta, lane);
   if (lane == 0 && gap < margin) {
     const int pos = atomicAdd(recheck_count, 1);
     recheck_list[pos] = t;
@@ -619,12 +648,17 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   hipError_t err = launch_router_logits(a, s);
   if (err != hipSuccess) return err;
-  router_centroid_norms<<<a.E, 256, 0, s>>>(a.wg, a.E, a.d, a.wn2);
   const int nb = cdiv(a.T, 4);
+  // the MFMA logits left the centroid norms and the token norms per slice of d; on the vector-ALU path
+  // the centroid norms come from their own pass and the top-K reads u
+  const bool mfma = a.u_bf16 && a.use_mfma;
+  if (!mfma) router_prep_wg<false><<<a.E, 256, 0, s>>>(a.wg, a.E, a.d, a.wn2, nullptr);
+  const float* un2 = mfma ? a.un2 : nullptr;
+  const int nsl = mfma ? router_mfma_slices(a.T, a.E, a.d) : 0;
   auto topk = [&](auto gate, auto* u) {
     constexpr int G = decltype(gate)::value;
     router_topk<G><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.n_groups, a.topk_groups, a.delta, u,
-                                      a.d, a.wn2, a.topk_idx, a.topk_w, a.recheck_count, a.recheck_list);
+                                      a.d, un2, nsl, a.wn2, a.topk_idx, a.topk_w, a.recheck_count, a.recheck_list);
   };
   using Softmax = std::integral_constant<int, MOE_GATE_SOFTMAX>;
   using Sigmoid = std::integral_constant<int, MOE_GATE_SIGMOID_BIAS>;
