@@ -135,7 +135,7 @@ Layout layout(const moe_config* c) {
   L.recheck_count = take(16);
   L.recheck_list = take(T * 4);
   L.wn2 = take(E * 4);
-  L.un2 = take(use_mfma_router(c) ? 4 * T * 4 : 0);
+  L.un2 = take((use_mfma_router(c) ? 4 : (size_t)ksplit) * T * 4);   // token norms per slice of d
   const size_t nch = dispatch_chunks(c->T);
   L.chunk_counts = take(nch * E * 4);
   L.chunk_base = take(nch * E * 4);

@@ -16,7 +16,7 @@ struct RouteArgs {
   int n_groups, topk_groups;   // group-limited routing (0: none)
   float delta;            // base recheck margin (scaled per token by the size of its partial sums)
   float* wn2;             // [E] squared centroid norms (scratch)
-  float* un2;             // [4, T] squared token norms per slice of d, written by the MFMA logits (scratch)
+  float* un2;             // [slices, T] squared token norms per slice of d, written by the logits (scratch)
   float* z;               // [T, E] fp32 logits
   double* z64;            // [T, E] fp64 logits of rechecked tokens (compacted); MFMA logits: first the
                           // fp32 partial sums of up to four slices of d ([T, E] x 16 bytes)

@@ -16,12 +16,14 @@ namespace moe {
 // The products of fp32 / bf16 inputs are exact in fp64 and accumulate in fp64 (same vector rate as
 // unpacked fp32); z is rounded to fp32 once. With few tokens (a decode step) blockIdx.z takes one slice
 // [z klen, (z + 1) klen) of d and stores its fp64 partial sum, and router_logits_sum adds the slices in
-// order, so the result does not depend on how the blocks are scheduled.
+// order, so the result does not depend on how the blocks are scheduled. Blocks of the first 64 experts
+// also add up the squares of their token rows over their slice (un2part[slice][t], for the recheck
+// margin; nullptr: not wanted).
 template <typename TU>
 __global__ __launch_bounds__(256) void router_logits_valu(const TU* __restrict__ u, const float* __restrict__ wg,
                                                           const float* __restrict__ off, int T, int E, int d,
                                                           int klen, float* __restrict__ z, double* __restrict__ zpart,
-                                                          int* __restrict__ recheck_count) {
+                                                          int* __restrict__ recheck_count, float* __restrict__ un2part) {
   __shared__ float As[32][68];
   __shared__ float Bs[32][68];
   const int tid = threadIdx.x;
@@ -31,6 +33,8 @@ __global__ __launch_bounds__(256) void router_logits_valu(const TU* __restrict__
   double acc[4][4] = {};
   const int lr = tid >> 2, lk = (tid & 3) * 8;
   const int kb = blockIdx.z * klen, ke = min(d, kb + klen);
+  const bool norms = un2part != nullptr && blockIdx.y == 0;
+  float sa = 0.f;                         // squares of this thread's pieces of token row t0 + lr
   for (int k0 = kb; k0 < ke; k0 += 32) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -43,6 +47,7 @@ __global__ __launch_bounds__(256) void router_logits_valu(const TU* __restrict__
       if (e0 + lr < E && k < ke) b = wg[(size_t)(e0 + lr) * d + k];
       As[lk + i][lr] = a;
       Bs[lk + i][lr] = b;
+      if (norms) sa = fmaf(a, a, sa);
     }
     __syncthreads();
 #pragma unroll 8
@@ -58,6 +63,12 @@ __global__ __launch_bounds__(256) void router_logits_valu(const TU* __restrict__
         for (int j = 0; j < 4; ++j) acc[i][j] = fma((double)a[i], (double)b[j], acc[i][j]);
     }
     __syncthreads();
+  }
+  if (norms) {
+    // the 4 threads 4 lr .. 4 lr + 3 hold the pieces of row lr
+    sa += __shfl_xor(sa, 1, 64);
+    sa += __shfl_xor(sa, 2, 64);
+    if ((tid & 3) == 0 && t0 + lr < T) un2part[(size_t)blockIdx.z * T + t0 + lr] = sa;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -271,23 +282,14 @@ void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s) {
 // which is at most |u_t| |e_i| (Cauchy-Schwarz). The base margin holds for |u_t| |e_i| up to sqrt(d) (token
 // rows of RMS 1 against centroids of norm 1); a token whose |u_t| max_i |e_i| is larger gets the margin
 // scaled by the ratio. wn2[i] = |e_i|^2 comes from router_prep_wg.
-// delta * max(1, |u_t| max_i |e_i| / sqrt(d)) for token t, on one wave. |u_t|^2 is the sum of the nsl
-// slice partials un2[s][t] the MFMA logits wrote, or (un2 == nullptr) is summed here from the row.
-template <typename TU>
-__device__ __forceinline__ float token_margin(const TU* __restrict__ ut, int d, const float* __restrict__ un2, int nsl,
-                                              int t, int T, const float* __restrict__ wn2, int E, float delta, int lane) {
+// delta * max(1, |u_t| max_i |e_i| / sqrt(d)) for token t, on one wave: |u_t|^2 is the sum of the nsl
+// slice partials un2[s][t] the logits kernels wrote (lane l takes slices l, l + 64, ..., then a fixed
+// reduction tree).
+__device__ __forceinline__ float token_margin(const float* __restrict__ un2, int nsl, int t, int T, int d,
+                                              const float* __restrict__ wn2, int E, float delta, int lane) {
   float su = 0.f;
-  if (un2) {
-    for (int sl = 0; sl < nsl; ++sl) su += un2[(size_t)sl * T + t];
-  } else {
-    for (int k = lane; k < d; k += 64) {
-      float v;
-      if constexpr (sizeof(TU) == 2) v = bf16_to_f32(ut[k]);
-      else v = ut[k];
-      su = fmaf(v, v, su);
-    }
-    su = wave_sum(su);
-  }
+  for (int sl = lane; sl < nsl; sl += 64) su += un2[(size_t)sl * T + t];
+  su = wave_sum(su);
   float wm = 0.f;
   for (int e = lane; e < E; e += 64) wm = fmaxf(wm, wn2[e]);
   wm = wave_max(wm);
@@ -382,10 +384,10 @@ __device__ __forceinline__ V group_limit_wave(const V key[4], bool valid[4], int
   return mth - m1;
 }
 
-template <int GATE, typename TU>
+template <int GATE>
 __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, int T, int E, int K,
                                                    const float* __restrict__ bias, int renorm, int G, int M,
-                                                   float delta, const TU* __restrict__ u, int d,
+                                                   float delta, int d,
                                                    const float* __restrict__ un2, int nsl, const float* __restrict__ wn2,
                                                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                    int* __restrict__ recheck_count, int* __restrict__ recheck_list) {
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, 
     topk_idx[(size_t)t * K + rank] = my_e;
     topk_w[(size_t)t * K + rank] = g;
   }
-  const float margin = token_margin(u + (size_t)t * d, d, un2, nsl, t, T, wn2, E, delta, lane);
+  const float margin = token_margin(un2, nsl, t, T, d, wn2, E, delta, lane);
   if (lane == 0 && gap < margin) {
     const int pos = atomicAdd(recheck_count, 1);
     recheck_list[pos] = t;
@@ -632,10 +634,10 @@ hipError_t launch_router_logits(const RouteArgs& a, hipStream_t s) {
   dim3 g1(cdiv(a.T, 64), cdiv(a.E, 64), split ? a.ksplit : 1);
   if (a.u_bf16)
     router_logits_valu<uint16_t><<<g1, 256, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.T, a.E, a.d, klen, a.z, zp,
-                                                    a.recheck_count);
+                                                    a.recheck_count, a.un2);
   else
     router_logits_valu<float><<<g1, 256, 0, s>>>((const float*)a.u, a.wg, a.off, a.T, a.E, a.d, klen, a.z, zp,
-                                                 a.recheck_count);
+                                                 a.recheck_count, a.un2);
   if (split) {
     const long long n = (long long)a.T * a.E;
     const long long nb = (n + 255) / 256;
@@ -649,28 +651,18 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   hipError_t err = launch_router_logits(a, s);
   if (err != hipSuccess) return err;
   const int nb = cdiv(a.T, 4);
-  // the MFMA logits left the centroid norms and the token norms per slice of d; on the vector-ALU path
-  // the centroid norms come from their own pass and the top-K reads u
+  // the logits kernels left the token norms per slice of d; the MFMA path also the centroid norms
   const bool mfma = a.u_bf16 && a.use_mfma;
   if (!mfma) router_prep_wg<false><<<a.E, 256, 0, s>>>(a.wg, a.E, a.d, a.wn2, nullptr);
-  const float* un2 = mfma ? a.un2 : nullptr;
-  const int nsl = mfma ? router_mfma_slices(a.T, a.E, a.d) : 0;
-  auto topk = [&](auto gate, auto* u) {
-    constexpr int G = decltype(gate)::value;
-    router_topk<G><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.n_groups, a.topk_groups, a.delta, u,
-                                      a.d, un2, nsl, a.wn2, a.topk_idx, a.topk_w, a.recheck_count, a.recheck_list);
-  };
-  using Softmax = std::integral_constant<int, MOE_GATE_SOFTMAX>;
-  using Sigmoid = std::integral_constant<int, MOE_GATE_SIGMOID_BIAS>;
-  const uint16_t* ub = static_cast<const uint16_t*>(a.u);
-  const float* uf = static_cast<const float*>(a.u);
-  if (a.gate == MOE_GATE_SOFTMAX) {
-    if (a.u_bf16) topk(Softmax{}, ub);
-    else topk(Softmax{}, uf);
-  } else {
-    if (a.u_bf16) topk(Sigmoid{}, ub);
-    else topk(Sigmoid{}, uf);
-  }
+  const int nsl = mfma ? router_mfma_slices(a.T, a.E, a.d) : a.ksplit;
+  if (a.gate == MOE_GATE_SOFTMAX)
+    router_topk<MOE_GATE_SOFTMAX><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.n_groups, a.topk_groups,
+                                                      a.delta, a.d, a.un2, nsl, a.wn2, a.topk_idx, a.topk_w,
+                                                      a.recheck_count, a.recheck_list);
+  else
+    router_topk<MOE_GATE_SIGMOID_BIAS><<<nb, 256, 0, s>>>(a.z, a.T, a.E, a.K, a.bias, a.renorm, a.n_groups,
+                                                           a.topk_groups, a.delta, a.d, a.un2, nsl, a.wn2, a.topk_idx,
+                                                           a.topk_w, a.recheck_count, a.recheck_list);
   if (a.u_bf16)
     router_recheck_logits<uint16_t><<<a.E, kRecheckThreads, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.E, a.d,
                                                                      a.recheck_count, a.recheck_list, a.z64);
