@@ -90,6 +90,7 @@ __global__ __launch_bounds__(256) void router_logits_sum(const double* __restric
   const size_t n = (size_t)T * E;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
     double acc = 0.0;
+#pragma unroll 8
     for (int s = 0; s < ksplit; ++s) acc += zpart[(size_t)s * n + i];
     z[i] = (float)(acc + (off ? (double)off[i % E] : 0.0));
   }
