@@ -38,20 +38,22 @@ hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_pr
 // than half of its bm rows are valid (both token halves of the block multiply), 69 or 62 otherwise (one
 // half multiplies; streaming its weights still takes most of the time). Within a range the blocks of
 // that XCD take tiles in order from a counter, then from the pool's.
-// Exclusive prefix sum over the 512 threads of a block (buf: 512 entries of LDS, reusable on return).
+// Exclusive prefix sum over the 512 threads of a block (buf: 512 entries of LDS, reusable on return):
+// a shuffle scan within each wave, then the totals of the waves before.
 __device__ __forceinline__ long long block_exclusive_scan(long long v, long long* buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int o = 1; o < 512; o <<= 1) {
-    const long long add = t >= o ? buf[t - o] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  long long x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
-  const long long incl = buf[t];
+  if (lane == 63) buf[wave] = x;
   __syncthreads();
-  return incl - v;
+  long long before = 0;
+  for (int w = 0; w < wave; ++w) before += buf[w];
+  __syncthreads();
+  return before + x - v;
 }
 
 // One thread per group (routed experts 0..E-1, the shared group E): its M tiles and the cost of one row
