@@ -103,3 +103,37 @@ def test_combine_skips_dropped_pairs(wdt):
                     torch.from_numpy(ys).to(H.DEV, ydt), torch.from_numpy(row_of).to(H.DEV), torch.from_numpy(w).to(H.DEV), h)
     torch.cuda.synchronize()
     assert np.array_equal(h.float().cpu().numpy(), ref)
+
+
+def test_combine_rounds_fp32_to_bf16_to_nearest_even():
+    """The combine's fp32 -> bf16 output rounding on every fp32 exponent with the low 16 mantissa bits below,
+    at and above the rounding midpoint (all 128 high-mantissa patterns, both signs), and on three whole
+    binades (around 1, the smallest normal, the largest subnormal): h = u + y_shared + 1 * y with u and
+    y_shared zero is bf16(y), compared with torch's round-to-nearest-even conversion on the CPU."""
+    d = 1024
+    hi = np.arange(256 * 128, dtype=np.uint32)            # exponent (8 bits) and top 7 mantissa bits
+    lows = np.array([0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    bits = ((hi[:, None] << 16) | lows[None, :]).reshape(-1)
+    whole = [((np.uint32(e) << 23) | np.arange(1 << 23, dtype=np.uint32)) for e in (127, 1, 0)]
+    bits = np.concatenate([bits] + whole)
+    bits = np.concatenate([bits, bits | np.uint32(0x80000000)])
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals) & (vals != 0)]
+    vals = vals[np.abs(vals.astype(np.float64)) < 3.3e38]   # beyond this bf16 rounds to infinity
+    T = -(-len(vals) // d)
+    y = np.zeros(T * d, dtype=np.float32)
+    y[:len(vals)] = vals
+    y = y.reshape(T, d)
+    print(f"[case] bf16 rounding, {len(vals)} values", flush=True)
+    cfg = moe.make_config(T, d, 1, 1, 1, 128, moe.MOE_GATE_SOFTMAX, 0, moe.MOE_BF16, moe.MOE_BF16)
+    zero_u = torch.zeros((T, d), dtype=torch.bfloat16, device=H.DEV)
+    zero_s = torch.zeros((T, d), dtype=torch.float32, device=H.DEV)
+    row_of = torch.arange(T, dtype=torch.int32, device=H.DEV).view(T, 1)
+    w = torch.ones((T, 1), dtype=torch.float32, device=H.DEV)
+    h = torch.empty((T, d), dtype=torch.bfloat16, device=H.DEV)
+    moe.moe_combine(cfg, zero_u, torch.from_numpy(y).to(H.DEV), zero_s, row_of, w, h)
+    torch.cuda.synchronize()
+    got = h.view(torch.int16).cpu().numpy().reshape(-1)[:len(vals)]
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy()
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, f"{bad.size} values round differently, e.g. {vals[bad[:4]]}"

@@ -84,3 +84,25 @@ def test_device_fill_matches_host_generator(dtype):
         assert np.array_equal(got, gen.f32_to_bf16_bits(ref))
     else:
         assert np.array_equal(t.cpu().numpy(), ref)
+
+
+def test_act_quantizer_every_fp32_value_in_range():
+    """Every fp32 value of magnitude in [2^-11, 448] (20 binades, both signs; below 2^-11 all round to zero)
+    through the device quantizer in rows of 127 values plus a 448, so the tile scale is exactly 1 and each
+    code is the plain E4M3 rounding of the fp32 input: the conversion is pinned at full fp32 resolution,
+    ties and subnormals included."""
+    m = np.arange(1 << 23, dtype=np.uint32)
+    for e in range(-11, 9):
+        x = ((np.uint32(127 + e) << 23) | m).view(np.float32)
+        x = x[np.abs(x) <= 448.0]
+        n = (len(x) // 127) * 127
+        # rows of 127; the last, partial row is filled up with values from the start of the binade
+        tail = [np.concatenate([x[n:], x[:127 - (len(x) - n)]])[None]] if len(x) > n else []
+        rows = np.concatenate([x[:n].reshape(-1, 127)] + tail, axis=0)
+        rows[1::2] = -rows[1::2]
+        tile = np.concatenate([rows, np.full((rows.shape[0], 1), 448.0, np.float32)], axis=1)
+        x32, q, s = _gpu_quant_act(np.ascontiguousarray(tile), False)
+        rq, rs = oquant.quantize_act_1x128(x32)
+        assert np.all(s == 1.0) and np.array_equal(rs, s), f"binade 2^{e}: scales"
+        bad = np.nonzero(q != rq)
+        assert bad[0].size == 0, f"binade 2^{e}: {bad[0].size} codes differ, first at {x32[bad][:4]}"
