@@ -38,8 +38,8 @@ def note(msg):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="v3_fp8")
     ap.add_argument("--tokens", type=int, default=0,
                     help="run the workload's layer with this many tokens instead (a sweep over batch sizes; the "
@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip timing the E4M3 expert backward")
     ap.add_argument("--no-subconfigs", action="store_true",
                     help="skip the timed runs of the other configurations (2B / 16B bf16 layers, V3 decode step)")
-    ap.add_argument("--sub-steps", type=int, default=200)
+    ap.add_argument("--sub-steps", type=int, default=300)
     ap.add_argument("--sub-warmup", type=int, default=20)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size kernel that profiler "
