@@ -100,10 +100,12 @@ __device__ __forceinline__ TileInfo decode_tile_lds(int id, const int32_t* mtp, 
   return ti;
 }
 
-// One K stage of one wave: its four 16-row weight tiles against its eight 16-token tiles. E4M3: every
-// 16x16x128 product is a fresh partial sum, scaled by (token scale x weight block scale) and added into
-// fp32 one MFMA after it is issued, so the matrix core and the vector ALU overlap.
-template <bool FP8, bool GATEUP, bool PACKED>
+// One K stage of one wave: its four 16-row weight tiles against its first JN 16-token tiles (the tiles of
+// its 128 tokens that hold rows of the M tile, rounded up to an even count; the others are neither read
+// nor multiplied). E4M3: every 16x16x128 product is a fresh partial sum, scaled by (token scale x weight
+// block scale) and added into fp32 one MFMA after it is issued, so the matrix core and the vector ALU
+// overlap.
+template <bool FP8, bool GATEUP, bool PACKED, int JN>
 __device__ __forceinline__ void mma_stage(f32x4 (&acc)[4][kTJ], const uint8_t* __restrict__ slot, int wn, int tok0,
                                           int tr, int g) {
   const uint8_t* A = slot;
@@ -148,11 +150,11 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[4][kTJ], const uint8_t* _
     [&]<int... J>(std::integer_sequence<int, J...>) {
       ([&] {
         constexpr int j = J;
-        if constexpr (j + 1 < kTJ) rd(B, tok0 + 16 * (j + 1) + tr, b[(j + 1) & 1][0], b[(j + 1) & 1][1]);
+        if constexpr (j + 1 < JN) rd(B, tok0 + 16 * (j + 1) + tr, b[(j + 1) & 1][0], b[(j + 1) & 1][1]);
         const i32x4 b0 = b[j & 1][0], b1 = b[j & 1][1];
         const i32x8 bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
         // token scales are read one 16-token tile ahead, like the token operand
-        if constexpr (j + 1 < kTJ) sxv[(j + 1) & 1] = SX[tok0 + 16 * (j + 1) + tr];
+        if constexpr (j + 1 < JN) sxv[(j + 1) & 1] = SX[tok0 + 16 * (j + 1) + tr];
         const float sx = sxv[j & 1];
         [&]<int... I>(std::integer_sequence<int, I...>) {
           ([&] {
@@ -165,13 +167,13 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[4][kTJ], const uint8_t* _
           }(), ...);
         }(std::make_integer_sequence<int, 4>{});
       }(), ...);
-    }(std::make_integer_sequence<int, kTJ>{});
-    acc[3][kTJ - 1] += cs[3] * p[1];
+    }(std::make_integer_sequence<int, JN>{});
+    acc[3][JN - 1] += cs[3] * p[1];
   } else {
     [&]<int... J>(std::integer_sequence<int, J...>) {
       ([&] {
         constexpr int j = J;
-        if constexpr (j + 1 < kTJ) rd(B, tok0 + 16 * (j + 1) + tr, b[(j + 1) & 1][0], b[(j + 1) & 1][1]);
+        if constexpr (j + 1 < JN) rd(B, tok0 + 16 * (j + 1) + tr, b[(j + 1) & 1][0], b[(j + 1) & 1][1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[i][0]),
@@ -180,7 +182,7 @@ __device__ __forceinline__ void mma_stage(f32x4 (&acc)[4][kTJ], const uint8_t* _
                                                               __builtin_bit_cast(bf16x8, b[j & 1][1]), acc[i][j], 0, 0, 0);
         }
       }(), ...);
-    }(std::make_integer_sequence<int, kTJ>{});
+    }(std::make_integer_sequence<int, JN>{});
   }
 }
 
@@ -360,13 +362,26 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
     for (int j = 0; j < kTJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   issue(lds);
-  for (int gs = 0;; ++gs) {
-    uint8_t* cur = lds + (gs & 1) * kSlot;
-    wait_vm0();       // this wave's copies of stage gs have landed
-    barrier_lds();    // ... and every wave's; every wave is done with the other slot
-    issue(lds + ((gs + 1) & 1) * kSlot);
-    if (tok0 < tc.nrows) mma_stage<FP8, GATEUP, PACKED>(acc, cur, wn, tok0, tr, g);
-    if (++kb < nst_c) continue;
+  int gs = 0;
+  for (;;) {
+    // the stages of tile tc, in a loop of their own for each count of live 16-token tiles of this wave
+    // (so that each loop holds one fully unrolled multiply)
+    auto stages = [&](auto jn) {
+      constexpr int JN = decltype(jn)::value;
+      for (; kb < nst_c; ++kb, ++gs) {
+        uint8_t* cur = lds + (gs & 1) * kSlot;
+        wait_vm0();       // this wave's copies of stage gs have landed
+        barrier_lds();    // ... and every wave's; every wave is done with the other slot
+        issue(lds + ((gs + 1) & 1) * kSlot);
+        if constexpr (JN > 0) mma_stage<FP8, GATEUP, PACKED, JN>(acc, cur, wn, tok0, tr, g);
+      }
+    };
+    const int live_rows = tc.nrows - tok0;
+    if (live_rows > 96) stages(std::integral_constant<int, 8>{});
+    else if (live_rows > 64) stages(std::integral_constant<int, 6>{});
+    else if (live_rows > 32) stages(std::integral_constant<int, 4>{});
+    else if (live_rows > 0) stages(std::integral_constant<int, 2>{});
+    else stages(std::integral_constant<int, 0>{});
 
     // ---- epilogue of tile tc. Lane holds, for token tok0 + 16 j + tr, channels 4 g + r of each 16-row
     // weight tile i (gate/up: gate channels 32 wn + 16 i for i < 2, their up channels for i >= 2).
