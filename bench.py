@@ -166,9 +166,16 @@ def time_backward(moe, L, w, ws, reps=5):
     if w.Ks > 0:
         tt["ws13"], tt["ws13s"] = tr(t["ws13"], t["ws13s"])
         tt["ws2"], tt["ws2s"] = tr(t["ws2"], t["ws2s"])
+    # the transposed weights in the tiled layout, like the forward's
+    for key, which in (("w13", moe.MOE_PACK_W13T), ("w2", moe.MOE_PACK_W2T), ("ws13", moe.MOE_PACK_WS13T),
+                       ("ws2", moe.MOE_PACK_WS2T)):
+        if key in tt:
+            tiled = torch.empty_like(tt[key])
+            moe.moe_pack_weights(L.cfg, which, tt[key], tiled)
+            tt[key] = tiled
     layer_t = moe.make_layer(tt["w13"], tt["w2"], t["wg"], ws13=tt.get("ws13"), ws2=tt.get("ws2"),
                              w13_scale=tt["w13s"], w2_scale=tt["w2s"], ws13_scale=tt.get("ws13s"),
-                             ws2_scale=tt.get("ws2s"))
+                             ws2_scale=tt.get("ws2s"), weight_layout=moe.MOE_LAYOUT_TILED)
     idx = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
     gw = torch.empty((w.T, w.K), dtype=torch.float32, device=dev)
     counts = torch.empty(w.E, dtype=torch.int32, device=dev)

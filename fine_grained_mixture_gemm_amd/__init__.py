@@ -19,7 +19,7 @@ __all__ = [
     "moe_balance_stats", "moe_backward_workspace_size", "moe_expert_ffn_backward_input", "moe_transpose_fp8_weights",
     "moe_expert_ffn_backward", "moe_forward_noalloc", "MOE_NOALLOC_SCRATCH_BYTES", "moe_route_margin",
     "moe_pack_weights", "MOE_LAYOUT_ROWS", "MOE_LAYOUT_TILED", "MOE_PACK_W13", "MOE_PACK_W2", "MOE_PACK_WS13",
-    "MOE_PACK_WS2",
+    "MOE_PACK_WS2", "MOE_PACK_W13T", "MOE_PACK_W2T", "MOE_PACK_WS13T", "MOE_PACK_WS2T",
 ]
 
 # always the in-tree build, next to this file
@@ -32,7 +32,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_BIAS = range(2)
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILED = range(2)
-MOE_PACK_W13, MOE_PACK_W2, MOE_PACK_WS13, MOE_PACK_WS2 = range(4)
+MOE_PACK_W13, MOE_PACK_W2, MOE_PACK_WS13, MOE_PACK_WS2, MOE_PACK_W13T, MOE_PACK_W2T, MOE_PACK_WS13T, MOE_PACK_WS2T = range(8)
 MARK_NAMES = ("route_begin", "route_end", "dispatch_end", "quant_end", "gateup_end", "down_end", "combine_end")
 MOE_NUM_MARKS = len(MARK_NAMES)
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",

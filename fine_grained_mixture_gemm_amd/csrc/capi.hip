@@ -723,9 +723,14 @@ moe_status moe_pack_weights(const moe_config* cfg, int32_t which, const void* sr
     case MOE_PACK_W2: groups = E; rows = d; cols = f; break;
     case MOE_PACK_WS13: groups = fs > 0 ? 1 : 0; rows = 2 * fs; cols = d; gateup = true; break;
     case MOE_PACK_WS2: groups = fs > 0 ? 1 : 0; rows = d; cols = fs; break;
+    case MOE_PACK_W13T: groups = E; rows = d; cols = 2 * f; break;
+    case MOE_PACK_W2T: groups = E; rows = f; cols = d; break;
+    case MOE_PACK_WS13T: groups = fs > 0 ? 1 : 0; rows = d; cols = 2 * fs; break;
+    case MOE_PACK_WS2T: groups = fs > 0 ? 1 : 0; rows = fs; cols = d; break;
     default: return fail(MOE_ERR_INVALID_ARG, "bad which %d", which);
   }
   if (groups == 0) return MOE_OK;
+  if (rows % 256) return fail(MOE_ERR_UNSUPPORTED, "the matrix has %d rows, not a multiple of 256", rows);
   if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "src / dst is NULL");
   if (src == dst) return fail(MOE_ERR_INVALID_ARG, "the layout change cannot run in place");
   // check_cfg has d % 256 == 0 and f % 128 == 0: gate/up tiles of 128 + 128 rows, down tiles of 256 rows,
@@ -749,8 +754,6 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
   MOE_TRY(check_bwd_cfg(cfg));
   MOE_TRY(check_layer_experts(cfg, layer));
   MOE_TRY(check_layer_experts(cfg, layer_t));
-  if (layer_t->weight_layout != MOE_LAYOUT_ROWS)
-    return fail(MOE_ERR_UNSUPPORTED, "layer_t (the transposed weights) must be in the row layout");
   const moe_config* c = cfg;
   const bool sh = c->n_shared > 0;
   const bool want_dx = dx_routed != nullptr, want_dw = dw13 != nullptr;
@@ -818,7 +821,7 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
   g.out_shared = base + L.gv_s;
   g.packed = layer->weight_layout == MOE_LAYOUT_TILED;
   MOE_TRY(hip_status(launch_gemm_mfma(g, true, true, grid, s, true), "g/v GEMM launch"));
-  g.packed = 0;   // the transposed weights below are row-major
+  g.packed = layer_t->weight_layout == MOE_LAYOUT_TILED;   // the transposed weights below
   // 2. dy quantized 1x128 along d; da = dy W2 (weights W2^T [f, d]: output f, contraction d), fp32
   MOE_TRY(hip_status(launch_quant_act(dy_routed, true, rows, d, base + L.dyq_r, F(L.dys_r), s), "dy quantization launch"));
   if (sh) MOE_TRY(hip_status(launch_quant_act(dy_shared, true, T, d, base + L.dyq_s, F(L.dys_s), s), "dy quantization launch"));

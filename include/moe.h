@@ -61,7 +61,12 @@ typedef enum {
 } moe_weight_layout;
 
 /* Which weight matrix moe_pack_weights converts. */
-typedef enum { MOE_PACK_W13 = 0, MOE_PACK_W2 = 1, MOE_PACK_WS13 = 2, MOE_PACK_WS2 = 3 } moe_pack_which;
+typedef enum {
+  MOE_PACK_W13 = 0, MOE_PACK_W2 = 1, MOE_PACK_WS13 = 2, MOE_PACK_WS2 = 3,
+  /* the transposed weights of the expert backward (moe_transpose_fp8_weights): each packed in tiles of
+   * 256 rows like W2 */
+  MOE_PACK_W13T = 4, MOE_PACK_W2T = 5, MOE_PACK_WS13T = 6, MOE_PACK_WS2T = 7
+} moe_pack_which;
 
 typedef struct {
   int32_t T;           /* tokens (>= 0; T == 0 is a no-op) */
@@ -225,8 +230,8 @@ moe_status moe_update_bias(const moe_config* cfg, const int32_t* counts, float g
  *  layer    the forward weights (w13, w13_scale, ws13, ws13_scale are used), in either layout.
  *  layer_t  the same weights transposed (moe_transpose_fp8_weights, from the row layout): w13 =
  *           [W1; W3]^T [E, d, 2f] with scales [E, d/128, 2f/128], w2 = W2^T [E, f, d] with scales
- *           [E, f/128, d/128]; ws13 / ws2 likewise for the shared block. Row layout only
- *           (MOE_ERR_UNSUPPORTED otherwise).
+ *           [E, f/128, d/128]; ws13 / ws2 likewise for the shared block. Either layout: MOE_LAYOUT_TILED
+ *           with w13, w2, ws13, ws2 packed by MOE_PACK_W13T, MOE_PACK_W2T, MOE_PACK_WS13T, MOE_PACK_WS2T.
  *  u [T, d] bf16 (the layer input), offsets / perm_src as moe_dispatch returns them.
  *  dy_routed [T*K, d] bf16, dy_shared [T, d] bf16 (n_shared == 1); dx_routed [T*K, d] bf16 out,
  *  dx_shared [T, d] bf16 out.
@@ -270,7 +275,9 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
  * Scales are not touched.
  *  cfg    bf16 or fp8 weights (the sizes come from it; its T is not used).
  *  which  MOE_PACK_W13 (src/dst [E, 2f, d]), MOE_PACK_W2 ([E, d, f]), MOE_PACK_WS13 ([2 Ks f, d]),
- *         MOE_PACK_WS2 ([d, Ks f]); the shared ones are a no-op when Ks == 0.
+ *         MOE_PACK_WS2 ([d, Ks f]); for the backward's transposed weights MOE_PACK_W13T ([E, d, 2f]),
+ *         MOE_PACK_W2T ([E, f, d]), MOE_PACK_WS13T ([d, 2 Ks f]), MOE_PACK_WS2T ([Ks f, d]), all in tiles
+ *         of 256 rows (f % 256 == 0 for W2T); the shared ones are a no-op when Ks == 0.
  *  src, dst  device buffers of the matrix's size, caller-owned, not overlapping (MOE_ERR_INVALID_ARG
  *         when src == dst).
  * Asynchronous on `stream`. */

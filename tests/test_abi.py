@@ -194,7 +194,9 @@ def test_weight_layout_argument_errors():
     cfg = _cfg()
     f32 = _cfg(act_dtype=moe.MOE_F32, w_dtype=moe.MOE_F32)
     assert lib.moe_pack_weights(ctypes.byref(f32), moe.MOE_PACK_W13, 16, 32, None) == moe.MOE_ERR_UNSUPPORTED
-    assert lib.moe_pack_weights(ctypes.byref(cfg), 4, 16, 32, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_pack_weights(ctypes.byref(cfg), 8, 16, 32, None) == moe.MOE_ERR_INVALID_ARG
+    # W2^T has f rows: the tiled layout needs a multiple of 256 (inter_dim 128 here)
+    assert lib.moe_pack_weights(ctypes.byref(cfg), moe.MOE_PACK_W2T, 16, 32, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_pack_weights(ctypes.byref(cfg), moe.MOE_PACK_W2, 16, 16, None) == moe.MOE_ERR_INVALID_ARG  # in place
     assert lib.moe_pack_weights(ctypes.byref(cfg), moe.MOE_PACK_W2, None, 16, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_pack_weights(ctypes.byref(_cfg(n_shared=0)), moe.MOE_PACK_WS13, None, None, None) == moe.MOE_OK

@@ -49,6 +49,10 @@ def test_pack_matches_definition(wdt):
     rng = np.random.default_rng(5)
     shapes = {moe.MOE_PACK_W13: (w.E, 2 * w.f, w.d), moe.MOE_PACK_W2: (w.E, w.d, w.f),
               moe.MOE_PACK_WS13: (1, 2 * w.fs, w.d), moe.MOE_PACK_WS2: (1, w.d, w.fs)}
+    if wdt == "fp8":
+        # the backward's transposed weights, in plain 256-row tiles
+        shapes.update({moe.MOE_PACK_W13T: (w.E, w.d, 2 * w.f), moe.MOE_PACK_W2T: (w.E, w.f, w.d),
+                       moe.MOE_PACK_WS13T: (1, w.d, 2 * w.fs), moe.MOE_PACK_WS2T: (1, w.fs, w.d)})
     for which, (G, R, C) in shapes.items():
         host = rng.integers(0, 256, size=(G, R, C * esz), dtype=np.uint8)
         src = torch.from_numpy(host).to(H.DEV)
@@ -106,7 +110,22 @@ def test_tiled_forward_is_bit_identical(name):
         assert torch.equal(a, b), f"{name}: {k} differs between the row and the tiled layout"
 
 
-def test_tiled_backward_input_is_bit_identical():
+def _tiled_transposed_layer(g, tt):
+    """The transposed weights of the backward (tt, row layout) copied into the tiled layout."""
+    out = {}
+    for key, which in (("w13", moe.MOE_PACK_W13T), ("w2", moe.MOE_PACK_W2T), ("ws13", moe.MOE_PACK_WS13T),
+                       ("ws2", moe.MOE_PACK_WS2T)):
+        if key in tt:
+            out[key] = _tiled_copy(g.cfg, which, tt[key])
+    torch.cuda.synchronize()
+    layer = moe.make_layer(out["w13"], out["w2"], g.t["wg"], ws13=out.get("ws13"), ws2=out.get("ws2"),
+                           w13_scale=tt["w13s"], w2_scale=tt["w2s"], ws13_scale=tt.get("ws13s"),
+                           ws2_scale=tt.get("ws2s"), weight_layout=moe.MOE_LAYOUT_TILED)
+    return layer, out
+
+
+def test_tiled_backward_is_bit_identical():
+    """Input and weight gradients with the forward and the transposed weights tiled, against both in rows."""
     from tests.test_gpu_backward import _bf16_normal, _transposed_layer
     w = W["v3_fp8"].replace(name="bwd_tiled", T=160, d=512, E=16, K=4)
     print("[case] bwd_tiled", flush=True)
@@ -114,17 +133,21 @@ def test_tiled_backward_input_is_bit_identical():
     layer_tiled = _tiled_layer(g)
     ws = H.workspace(g)
     o = H.run_stages(g, ws)
-    layer_t, _tt = _transposed_layer(g)
+    layer_t, tt = _transposed_layer(g)
+    layer_t_tiled, _keep = _tiled_transposed_layer(g, tt)
     rng = np.random.default_rng(11)
     dy_r, _ = _bf16_normal(rng, (w.T * w.K, w.d))
     dy_s, _ = _bf16_normal(rng, (w.T, w.d))
     bws = torch.empty(moe.moe_backward_workspace_size(g.cfg), dtype=torch.uint8, device=H.DEV)
+    bf = dict(dtype=torch.bfloat16, device=H.DEV)
     res = []
-    for layer in (g.layer, layer_tiled):
-        dx_r = torch.empty((w.T * w.K, w.d), dtype=torch.bfloat16, device=H.DEV)
-        dx_s = torch.empty((w.T, w.d), dtype=torch.bfloat16, device=H.DEV)
-        moe.moe_expert_ffn_backward_input(g.cfg, layer, layer_t, g.t["u"], o["offsets"], o["perm"], dy_r, dy_s, dx_r,
-                                          dx_s, bws)
+    for layer, lt in ((g.layer, layer_t), (layer_tiled, layer_t_tiled), (layer_tiled, layer_t)):
+        out = [torch.empty((w.T * w.K, w.d), **bf), torch.empty((w.T, w.d), **bf),
+               torch.empty((w.E, 2 * w.f, w.d), **bf), torch.empty((w.E, w.d, w.f), **bf),
+               torch.empty((2 * w.fs, w.d), **bf), torch.empty((w.d, w.fs), **bf)]
+        moe.moe_expert_ffn_backward(g.cfg, layer, lt, g.t["u"], o["offsets"], o["perm"], dy_r, dy_s, *out, bws)
         torch.cuda.synchronize()
-        res.append((dx_r.view(torch.int16).cpu(), dx_s.view(torch.int16).cpu()))
-    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1]), "dx differs between the layouts"
+        res.append([x.view(torch.int16).cpu() for x in out])
+    for k in (1, 2):
+        for i, nm in enumerate(("dx_r", "dx_s", "dw13", "dw2", "dws13", "dws2")):
+            assert torch.equal(res[0][i], res[k][i]), f"{nm} differs between the layouts (case {k})"
