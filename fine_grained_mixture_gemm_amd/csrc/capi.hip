@@ -107,7 +107,7 @@ moe_status check_cfg(const moe_config* c) {
 struct Layout {
   size_t z, z64, wg_split, zpart, recheck_count, recheck_list, wn2, un2;
   size_t chunk_counts, chunk_base, mt_prefix, xsched;
-  size_t uq, us, a_r, a_s, as_r, as_s;
+  size_t uq, us, xsb_r, xsb_s, a_r, a_s, as_r, as_s;
   size_t f_idx, f_w, f_counts, f_offsets, f_perm, f_rowof, f_yr, f_ys;
   size_t bal_psum, bal_cnt, bal_seqp, bal_seqn, bal_seq;
   size_t total;
@@ -143,6 +143,11 @@ Layout layout(const moe_config* c) {
   L.xsched = take(2 * (kSchedRange + kSchedCount) * 4);
   L.uq = take(fp8 ? T * d : 0);
   L.us = take(fp8 ? T * (d / 128) * 4 : 0);
+  // the same scales block-major in the dispatched order (routed rows) and in token order (shared experts),
+  // read by the matrix-core gate/up GEMM
+  const bool xsb = fp8 && use_mfma_gemm(c) && c->T > gemm_decode_max_tokens();
+  L.xsb_r = take(xsb ? rows * (d / 128) * 4 : 0);
+  L.xsb_s = take(xsb && fs > 0 ? T * (d / 128) * 4 : 0);
   L.a_r = take(rows * f * esz_a);
   L.a_s = take(T * fs * esz_a);
   L.as_r = take(fp8 ? rows * (f / 128) * 4 : 0);
@@ -436,6 +441,20 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
     xin = base + L.uq;
     xs = reinterpret_cast<const float*>(base + L.us);
   }
+  // matrix-core E4M3 path: token scales and the scales of a block-major (one stage's scales of a tile are
+  // contiguous)
+  const bool xsb = fp8 && mfma && !decode;
+  const long long rows = (long long)c->T * c->top_k;
+  if (xsb) {
+    const int kblk = c->d_model / 128;
+    MOE_TRY(hip_status(launch_scales_by_block(xs, kblk, perm, offsets + c->n_routed, (int)rows,
+                                              reinterpret_cast<float*>(base + L.xsb_r), (int)rows, s),
+                       "scale layout launch"));
+    if (fs > 0)
+      MOE_TRY(hip_status(launch_scales_by_block(xs, kblk, nullptr, nullptr, c->T, reinterpret_cast<float*>(base + L.xsb_s),
+                                                c->T, s),
+                         "scale layout launch"));
+  }
   mark(MOE_MARK_QUANT_END, s);
   // gate/up + SwiGLU
   g.w_routed = static_cast<const uint8_t*>(l->w13);
@@ -444,13 +463,14 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   g.ws_shared = l->ws13_scale;
   g.x_routed = xin;
   g.x_shared = xin;
-  g.xs_routed = xs;
-  g.xs_shared = xs;
+  g.xs_routed = xsb ? reinterpret_cast<const float*>(base + L.xsb_r) : xs;
+  g.xs_shared = xsb ? reinterpret_cast<const float*>(base + L.xsb_s) : xs;
+  g.xs_ld_routed = g.os_ld_routed = xsb ? (int)rows : 0;
+  g.xs_ld_shared = g.os_ld_shared = xsb ? c->T : 0;
   g.out_routed = base + L.a_r;
   g.out_shared = base + L.a_s;
   g.out_scale_routed = reinterpret_cast<float*>(base + L.as_r);
   g.out_scale_shared = reinterpret_cast<float*>(base + L.as_s);
-  const long long rows = (long long)c->T * c->top_k;
   if (decode) {
     MOE_TRY(hip_status(launch_gemm_decode(g, true, s), "gate/up GEMM launch"));
   } else if (mfma) {

@@ -256,6 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
   int nst_l = 0, kl = 0, kblk_l = 0, kbytes_l = 0, fg_l = 0, started = 1;
   bool live = true;
   uint32_t boff[kChunks], sxoff = 0;
+  int sxstep = 1;
   auto setup = [&]() {
     tl = tn;
     const bool shared = tl.group == E;
@@ -282,7 +283,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
     }
     if (FP8) {
       const int r = gather ? rawn[kChunks] : tl.rowbase + row_in_tile(tl, kChunks);
-      sxoff = (uint32_t)r * kblk_l;
+      const int xs_ld = shared ? a.xs_ld_shared : a.xs_ld_routed;
+      // block-major scales are read in the dispatched order (row rowbase + i), not through perm_src
+      sxoff = xs_ld ? (uint32_t)(tl.rowbase + row_in_tile(tl, kChunks)) : (uint32_t)r * kblk_l;
+      sxstep = xs_ld ? xs_ld : 1;
       // lane 0 of wave 4 copies the scale of block row c0 / 128 (gate, or the first 128 down rows),
       // lane 1 that of (fg + c0) / 128 (up) or c0 / 128 + 1 (the next 128 down rows)
       const int c0 = tl.n_tile * (GATEUP ? 128 : kBW);
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
 #pragma unroll
     for (int q = 0; q < kChunks; ++q)
       if (q == 0 || 64 * q < tl.nrows) dma16(Xk + boff[q], sl + kSlotA + (q * kThreads + wave * 64) * 16);
-    if (FP8 && wave < 4) dma4(XSl + sxoff + kk, sl + kSX + wave * 256);
+    if (FP8 && wave < 4) dma4(XSl + sxoff + (size_t)kk * sxstep, sl + kSX + wave * 256);
     if (FP8 && wave == 4 && lane < 2) dma4(WSl + kk, sl + kWS);
   };
 
@@ -437,7 +441,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
           float s, inv;
           e4m3_scales(m, s, inv);
           if (tok < tc.nrows) {
-            if (wn == 0 && g == 0) OS[(size_t)(tc.rowbase + tok) * (fg / 128) + tc.n_tile] = s;
+            if (wn == 0 && g == 0) {
+              const int os_ld = shared ? a.os_ld_shared : a.os_ld_routed;
+              OS[os_ld ? (size_t)tc.n_tile * os_ld + tc.rowbase + tok : (size_t)(tc.rowbase + tok) * (fg / 128) + tc.n_tile] = s;
+            }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
               *reinterpret_cast<uint32_t*>(OUT + (size_t)tok * out_stride + 16 * i) =

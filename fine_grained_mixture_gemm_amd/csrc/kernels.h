@@ -107,6 +107,10 @@ struct GemmArgs {
   float* out_scale_routed;    // gate/up fp8: scales of a
   float* out_scale_shared;
   int packed;                 // weights in the tiled layout of launch_pack_weights (matrix-core kernels only)
+  // Matrix-core kernels, E4M3: layout of the token scales. 0: [rows][kblk] (row r, block kb at r * kblk + kb);
+  // ld > 0: [kblk][ld] (at kb * ld + r), so that one stage's scales of a tile's consecutive rows are contiguous.
+  int xs_ld_routed, xs_ld_shared;
+  int os_ld_routed, os_ld_shared;   // the same choice for the scales of a written by the gate/up epilogue
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
@@ -115,6 +119,10 @@ void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 int dispatch_chunks(int T);
 hipError_t launch_quant_act(const void* x, bool x_bf16, int rows, int cols, uint8_t* q, float* scales, hipStream_t s);
+// out[kb * ld + r] = xs[src(r) * kblk + kb] for r < n, src(r) = perm[r] (perm non-null; n = *n_rows, the
+// dispatched row count, at most rows) or r (perm null; n = rows): the 1x128 scales of gathered rows, block-major.
+hipError_t launch_scales_by_block(const float* xs, int kblk, const int32_t* perm, const int32_t* n_rows, int rows,
+                                  float* out, int ld, hipStream_t s);
 hipError_t launch_quant_weight(const float* w, int batch, int rows, int cols, uint8_t* q, float* scales, hipStream_t s);
 hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_prefix, hipStream_t s);
 // M-tile prefix plus, for the gate/up (k = 0) and down (k = 1) launches of the matrix-core GEMM, the

@@ -83,6 +83,40 @@ __global__ __launch_bounds__(256) void quant_weight_128x128(const float* __restr
   if (threadIdx.x == 0) scales[(size_t)mat * nrb * ncb + (size_t)rb * ncb + cb] = s;
 }
 
+// 64 rows per block: their scales are read row by row (contiguous) into LDS and written block by block.
+__global__ __launch_bounds__(256) void scales_by_block(const float* __restrict__ xs, int kblk,
+                                                       const int32_t* __restrict__ perm, const int32_t* __restrict__ n_rows,
+                                                       int rows, float* __restrict__ out, int ld) {
+  __shared__ float tile[64][65];
+  __shared__ int src[64];
+  const int r0 = blockIdx.x * 64;
+  const int n = perm ? min(*n_rows, rows) : rows;
+  if (r0 >= n) return;
+  const int nr = min(64, n - r0);
+  if (threadIdx.x < nr) src[threadIdx.x] = perm ? perm[r0 + threadIdx.x] : r0 + threadIdx.x;
+  __syncthreads();
+  for (int kb0 = 0; kb0 < kblk; kb0 += 64) {
+    const int kc = min(64, kblk - kb0);
+    for (int i = threadIdx.x; i < nr * kc; i += 256) {
+      const int rr = i / kc, kb = i - rr * kc;
+      tile[rr][kb] = xs[(size_t)src[rr] * kblk + kb0 + kb];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * kc; i += 256) {
+      const int kb = i >> 6, rr = i & 63;
+      if (rr < nr) out[(size_t)(kb0 + kb) * ld + r0 + rr] = tile[rr][kb];
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_scales_by_block(const float* xs, int kblk, const int32_t* perm, const int32_t* n_rows, int rows,
+                                  float* out, int ld, hipStream_t s) {
+  if (rows == 0 || kblk == 0) return hipSuccess;
+  scales_by_block<<<(rows + 63) / 64, 256, 0, s>>>(xs, kblk, perm, n_rows, rows, out, ld);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_act(const void* x, bool x_bf16, int rows, int cols, uint8_t* q, float* scales, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const long long groups = (long long)rows * (cols / 128);
