@@ -29,13 +29,21 @@ struct RouteArgs {
   float* topk_w;
 };
 
-// Slices of d for the MFMA router logits: enough for about 512 blocks of 128 tokens x 64 experts (two
-// per CU of the chip's 256) when one slice gives fewer, at most four, each slice at least 8 stages of
-// 64 (at the V3 shape, 256 blocks: two slices; three slices there measured slower than two).
+// Block shape of the MFMA router logits: 256 tokens x 128 experts when four slices of d give at least one
+// block per CU of the chip's 256, else 128 tokens x 64 experts.
+inline bool router_mfma_large(int T, int E) {
+  return (long long)((T + 255) / 256) * ((E + 127) / 128) * 4 >= 256;
+}
+
+// Slices of d for the MFMA router logits, at most four, each at least 8 stages of 64: for the small
+// blocks enough for about 512 (two per CU; at the V3 shape with them, 256 blocks: two slices, three
+// measured slower), for the large ones about 256 (one per CU: 8 waves).
 inline int router_mfma_slices(int T, int E, int d) {
-  const long long blocks = (long long)((T + 127) / 128) * ((E + 63) / 64);
+  const bool large = router_mfma_large(T, E);
+  const long long blocks = large ? (long long)((T + 255) / 256) * ((E + 127) / 128)
+                                 : (long long)((T + 127) / 128) * ((E + 63) / 64);
   if (blocks <= 0) return 1;
-  long long ks = 512 / blocks;
+  long long ks = (large ? 256 : 512) / blocks;
   ks = ks < 1 ? 1 : (ks > 4 ? 4 : ks);
   while (ks > 1 && d / 64 < 8 * ks) --ks;
   return (int)ks;

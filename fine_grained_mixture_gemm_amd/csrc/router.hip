@@ -131,113 +131,130 @@ __global__ __launch_bounds__(256) void router_prep_wg(const float* __restrict__ 
   if (threadIdx.x == 0) wn2[e] = (part[0] + part[1]) + (part[2] + part[3]);
 }
 
-// 128 tokens x 64 experts per block; wave w owns experts 16w..16w+15 against all 128 tokens.
-// Tokens are staged 64 elements (128 bytes) at a time in a double-buffered XOR-swizzled LDS tile;
-// the centroid parts stream from global memory into registers. blockIdx.z takes the slice
+// 16 TJ tokens x 16 NW experts per block (NW waves); wave w owns experts 16w..16w+15 against all the
+// block's tokens. Tokens are staged 64 elements (128 bytes) at a time in a double-buffered XOR-swizzled LDS
+// tile; the centroid parts stream from global memory into registers. blockIdx.z takes the slice
 // [z klen, (z + 1) klen) of d: with one slice the kernel writes z = sum + off, with several it writes
 // the slice's fp32 partial sum to zpart[z] and router_logits_sum32 adds the slices in order.
-// Blocks of the first 64 experts also add up the squares of their token rows over their slice of d
+// Blocks of the first expert tile also add up the squares of their token rows over their slice of d
 // (un2part[slice][t], for the recheck margin; nullptr: not wanted).
-__global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ u, const uint16_t* __restrict__ parts,
-                                                          const float* __restrict__ off, int T, int E, int d,
-                                                          int klen, float* __restrict__ z, float* __restrict__ zpart,
-                                                          int* __restrict__ recheck_count, float* __restrict__ un2part) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][128 * 128];
+// Two shapes: 128 tokens x 64 experts (4 waves), and for large batches 256 tokens x 128 experts (8 waves),
+// which reads half the tokens and centroid parts from L2 per product.
+template <int TJ, int NW, int PF>
+__global__ __launch_bounds__(64 * NW) void router_logits_mfma(const uint16_t* __restrict__ u, const uint16_t* __restrict__ parts,
+                                                             const float* __restrict__ off, int T, int E, int d,
+                                                             int klen, float* __restrict__ z, float* __restrict__ zpart,
+                                                             int* __restrict__ recheck_count, float* __restrict__ un2part) {
+  constexpr int kTM = 16 * TJ, kThr = 64 * NW;
+  constexpr int kQ = kTM * 8 / kThr;   // 16-byte token pieces per thread per stage
+  static_assert(kQ * kThr == kTM * 8 && TJ % 8 == 0, "token staging");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kTM * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * 128, e0 = blockIdx.y * 64;
+  const int t0 = blockIdx.x * kTM, e0 = blockIdx.y * (16 * NW);
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *recheck_count = 0;
   const size_t n = (size_t)E * d;
   const int s0 = blockIdx.z * (klen / 64), nst = min(d, (int)(blockIdx.z + 1) * klen) / 64 - s0;
   const int erow = min(e0 + 16 * wave + (lane & 15), E - 1);
   const uint8_t* wp = reinterpret_cast<const uint8_t*>(parts + (size_t)erow * d) + 16 * (lane >> 4) + 128 * s0;
   const uint8_t* ub = reinterpret_cast<const uint8_t*>(u);
-  uint32_t boff[4];
+  uint32_t boff[kQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int id16 = q * 256 + tid;
+  for (int q = 0; q < kQ; ++q) {
+    const int id16 = q * kThr + tid;
     const int tok = min(t0 + (id16 >> 3), T - 1);
     boff[q] = (uint32_t)tok * (uint32_t)d * 2u + (id16 & 7) * 16 + 128u * s0;
   }
-  f32x4 acc[8];
+  f32x4 acc[TJ];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  i32x4 Bst[4];
+  for (int j = 0; j < TJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Tokens and centroid parts are loaded PF stages ahead (1 or 2) into two register sets used by even and
+  // odd stages (the loop below takes stages in pairs, so each set stays in fixed registers).
+  auto load_tokens = [&](int kb, i32x4 (&B)[kQ]) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) Bst[q] = *reinterpret_cast<const i32x4*>(ub + boff[q]);
-  // centroid parts of the next stage are loaded while this stage multiplies
-  i32x4 A[3][2], An[3][2];
+    for (int q = 0; q < kQ; ++q) B[q] = *reinterpret_cast<const i32x4*>(ub + (size_t)kb * 128 + boff[q]);
+  };
+  auto load_parts = [&](int kb, i32x4 (&A)[3][2]) {
 #pragma unroll
-  for (int p = 0; p < 3; ++p) {
-    A[p][0] = *reinterpret_cast<const i32x4*>(wp + p * n * 2);
-    A[p][1] = *reinterpret_cast<const i32x4*>(wp + p * n * 2 + 64);
-  }
+    for (int p = 0; p < 3; ++p) {
+      const uint8_t* pp = wp + p * n * 2 + (size_t)kb * 128;
+      A[p][0] = *reinterpret_cast<const i32x4*>(pp);
+      A[p][1] = *reinterpret_cast<const i32x4*>(pp + 64);
+    }
+  };
   const int tr = lane & 15, g = lane >> 4;
   const bool norms = un2part != nullptr && blockIdx.y == 0;
-  float su[4] = {0.f, 0.f, 0.f, 0.f};      // squares of this thread's 8-element pieces of rows 32 q + tid / 8
-  for (int kb = 0; kb < nst; ++kb) {
+  float su[kQ];   // squares of this thread's 8-element pieces of rows (q kThr + tid) / 8
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) su[q] = 0.f;
+  i32x4 B0[kQ], B1[kQ], A0[3][2], A1[3][2];
+  load_tokens(0, B0);
+  load_parts(0, A0);
+  if (PF == 2 && nst > 1) {
+    load_tokens(1, B1);
+    load_parts(1, A1);
+  }
+  // B, A: this stage's sets; Bn, An: the next stage's
+  auto stage = [&](int kb, i32x4 (&B)[kQ], i32x4 (&A)[3][2], i32x4 (&Bn)[kQ], i32x4 (&An)[3][2]) {
     uint8_t* buf = lds[kb & 1];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int id16 = q * 256 + tid, row = id16 >> 3, c = id16 & 7;
-      *reinterpret_cast<i32x4*>(buf + row * 128 + ((c ^ (row & 7)) * 16)) = Bst[q];
+    for (int q = 0; q < kQ; ++q) {
+      const int id16 = q * kThr + tid, row = id16 >> 3, c = id16 & 7;
+      *reinterpret_cast<i32x4*>(buf + row * 128 + ((c ^ (row & 7)) * 16)) = B[q];
       if (norms) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float lo = __uint_as_float((uint32_t)Bst[q][i] << 16), hi = __uint_as_float((uint32_t)Bst[q][i] & 0xFFFF0000u);
+          const float lo = __uint_as_float((uint32_t)B[q][i] << 16), hi = __uint_as_float((uint32_t)B[q][i] & 0xFFFF0000u);
           su[q] = fmaf(hi, hi, fmaf(lo, lo, su[q]));
         }
       }
     }
     __syncthreads();
-    if (kb + 1 < nst) {
+    if (PF == 2 && kb + 2 < nst) load_tokens(kb + 2, B);
+    if (PF == 1 && kb + 1 < nst) {
+      load_tokens(kb + 1, Bn);
+      load_parts(kb + 1, An);
+    }
+    // groups of eight token tiles; within a group the tiles are innermost, so consecutive MFMAs update
+    // different accumulators
 #pragma unroll
-      for (int q = 0; q < 4; ++q) Bst[q] = *reinterpret_cast<const i32x4*>(ub + (size_t)(kb + 1) * 128 + boff[q]);
+    for (int j0 = 0; j0 < TJ; j0 += 8) {
+      i32x4 b[8][2];
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        const uint8_t* pp = wp + p * n * 2 + (kb + 1) * 128;
-        An[p][0] = *reinterpret_cast<const i32x4*>(pp);
-        An[p][1] = *reinterpret_cast<const i32x4*>(pp + 64);
+      for (int j = 0; j < 8; ++j) {
+        const int row = 16 * (j0 + j) + tr;
+        b[j][0] = *reinterpret_cast<const i32x4*>(buf + row * 128 + ((g ^ (row & 7)) * 16));
+        b[j][1] = *reinterpret_cast<const i32x4*>(buf + row * 128 + (((4 + g) ^ (row & 7)) * 16));
       }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            acc[j0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[p][h]),
+                                                                  __builtin_bit_cast(bf16x8, b[j][h]), acc[j0 + j], 0, 0, 0);
     }
-    i32x4 b[8][2];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 16 * j + tr;
-      b[j][0] = *reinterpret_cast<const i32x4*>(buf + row * 128 + ((g ^ (row & 7)) * 16));
-      b[j][1] = *reinterpret_cast<const i32x4*>(buf + row * 128 + (((4 + g) ^ (row & 7)) * 16));
-    }
-    // the eight token tiles innermost: consecutive MFMAs update different accumulators
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int p = 0; p < 3; ++p)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[p][h]),
-                                                           __builtin_bit_cast(bf16x8, b[j][h]), acc[j], 0, 0, 0);
-    if (kb + 1 < nst) {
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        A[p][0] = An[p][0];
-        A[p][1] = An[p][1];
-      }
-    }
+    if (PF == 2 && kb + 2 < nst) load_parts(kb + 2, A);
+  };
+  for (int kb = 0; kb < nst; kb += 2) {
+    stage(kb, B0, A0, B1, A1);
+    if (kb + 1 < nst) stage(kb + 1, B1, A1, B0, A0);
   }
   if (norms) {
     // the 8 threads tid & ~7 .. tid | 7 hold the pieces of one row
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kQ; ++q) {
       float v = su[q];
       v += __shfl_xor(v, 1, 64);
       v += __shfl_xor(v, 2, 64);
       v += __shfl_xor(v, 4, 64);
-      const int t = t0 + 32 * q + (tid >> 3);
+      const int t = t0 + (q * kThr + tid) / 8;
       if ((tid & 7) == 0 && t < T) un2part[(size_t)blockIdx.z * T + t] = v;
     }
   }
   // lane holds experts 16 wave + 4 (lane >> 4) + r for token 16 j + (lane & 15)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < TJ; ++j) {
     const int t = t0 + 16 * j + (lane & 15);
     if (t >= T) continue;
 #pragma unroll
@@ -268,9 +285,15 @@ void launch_router_logits_mfma(const RouteArgs& a, hipStream_t s) {
   const int ks = router_mfma_slices(a.T, a.E, a.d);
   const int klen = cdiv(a.d / 64, ks) * 64;
   float* zp = ks > 1 ? reinterpret_cast<float*>(a.z64) : nullptr;
-  dim3 grid(cdiv(a.T, 128), cdiv(a.E, 64), ks);
-  router_logits_mfma<<<grid, 256, 0, s>>>((const uint16_t*)a.u, a.wg_split, a.off, a.T, a.E, a.d, klen, a.z, zp,
-                                          a.recheck_count, a.un2);
+  if (router_mfma_large(a.T, a.E)) {
+    dim3 grid(cdiv(a.T, 256), cdiv(a.E, 128), ks);
+    router_logits_mfma<16, 8, 2><<<grid, 512, 0, s>>>((const uint16_t*)a.u, a.wg_split, a.off, a.T, a.E, a.d, klen, a.z,
+                                                   zp, a.recheck_count, a.un2);
+  } else {
+    dim3 grid(cdiv(a.T, 128), cdiv(a.E, 64), ks);
+    router_logits_mfma<8, 4, 1><<<grid, 256, 0, s>>>((const uint16_t*)a.u, a.wg_split, a.off, a.T, a.E, a.d, klen, a.z,
+                                                  zp, a.recheck_count, a.un2);
+  }
   if (ks > 1) {
     const long long nz = (long long)a.T * a.E;
     const long long nb = (nz + 255) / 256;

@@ -161,6 +161,38 @@ def test_full_size_float_configs(name):
     print(name, _check_all(g, o, ref))
 
 
+# Batches large enough for the 256-token x 128-expert MFMA logits blocks (about 256 blocks over four slices
+# of d), with a ragged last token block (8000 = 31.25 x 256) and an expert count that is not a multiple of
+# 128, softmax and sigmoid + bias keys, and heavy-tailed rows for the sigmoid case: routing bit for bit
+# against the oracle, the fp32 keys inside the recheck margins.
+ROUTER_LARGE = {
+    "softmax": W["dsmoe2b_bf16"].replace(name="router_large_softmax", T=8000, d=2048, E=200, K=6, f=128),
+    "sigmoid_tail": W["v3_fp8"].replace(name="router_large_sigmoid_tail", T=8000, d=2048, E=200, K=8, f=128,
+                                        wdt="bf16", u_tail=True),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTER_LARGE))
+def test_router_large_blocks_ragged(name):
+    import fine_grained_mixture_gemm_amd as moe
+    w = ROUTER_LARGE[name]
+    # the library takes the large blocks when ceil(T / 256) ceil(E / 128) x 4 slices >= 256
+    assert -(-w.T // 256) * -(-w.E // 128) * 4 >= 256
+    print(f"[case] router large blocks {name}", flush=True)
+    g = H.build(w, keep_host_weights=False)
+    ws = H.workspace(g, poison=True)
+    idx = torch.empty((w.T, w.K), dtype=torch.int32, device="cuda")
+    gw = torch.empty((w.T, w.K), dtype=torch.float32, device="cuda")
+    moe.moe_route(g.cfg, g.layer, g.t["u"], g.t["bias"], idx, gw, ws)
+    z = torch.empty((w.T, w.E), dtype=torch.float32, device="cuda")
+    moe.moe_router_logits(g.cfg, g.layer, g.t["u"], z, ws)
+    torch.cuda.synchronize()
+    zr, r = H.oracle_route(g)
+    assert np.array_equal(H.to_np(idx), r["idx"]), "routing differs"
+    assert np.abs(H.to_np(gw) - r["w"]).max() < 1e-5
+    H.check_key_margins(g, H.to_np(z), r["key"], r["gap"], name)
+
+
 # E4M3 with the smallest inner dim f = 128: a row of a is one 1x128 tile, so one requantized code of a
 # that rounds the other way moves that row of y by about 0.3 * 3 / sqrt(128) = 8 % of its RMS, above the
 # 6e-2 bar. Such a code is one whose input window (the gate/up GEMM's fp32 summation bound carried through
