@@ -57,49 +57,6 @@ constexpr int kIds = kTab + 2 * kMaxGroups * 4 + 8;   // ring of the block's nex
 constexpr int kLdsBytes = kIds + 16;
 static_assert(kBW == kBM && kChunks == 4 && kLdsBytes <= 160 * 1024, "geometry");
 
-// Tile id -> (group, N tile, rows), from LDS copies of mt_prefix and offsets: routed experts ascending,
-// M index fastest within an expert (the M tiles of one N tile share its weight rows: blocks that take
-// them together start on the same weight stream, so later ones often find it in the XCD's L2), then the
-// shared group in the same order.
-__device__ __forceinline__ TileInfo decode_tile_lds(int id, const int32_t* mtp, const int32_t* off, int E, int T,
-                                                    int nt_r, int nt_s) {
-  TileInfo ti;
-  const int routed_tiles = mtp[E] * nt_r;
-  if (id < routed_tiles) {
-    int lo = 0, hi = E;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (mtp[mid] * nt_r <= id) lo = mid;
-      else hi = mid - 1;
-    }
-    const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int local = id - mtp[e] * nt_r;
-    ti.group = e;
-    const int mt_e = mtp[e + 1] - mtp[e];
-    ti.n_tile = local / mt_e;
-    const int m_tile = local - ti.n_tile * mt_e;
-    const int o0 = off[e], n_e = off[e + 1] - o0;
-    ti.row0 = m_tile * kBM;
-    ti.nrows = min(kBM, n_e - ti.row0);
-    ti.rowbase = o0 + ti.row0;
-  } else {
-    const int local = id - routed_tiles;
-    ti.group = E;
-    const int mt_s = (T + kBM - 1) / kBM;
-    ti.n_tile = local / mt_s;
-    const int m_tile = local - ti.n_tile * mt_s;
-    ti.row0 = m_tile * kBM;
-    ti.nrows = min(kBM, T - ti.row0);
-    ti.rowbase = ti.row0;
-  }
-  ti.group = __builtin_amdgcn_readfirstlane(ti.group);
-  ti.n_tile = __builtin_amdgcn_readfirstlane(ti.n_tile);
-  ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
-  ti.nrows = __builtin_amdgcn_readfirstlane(ti.nrows);
-  ti.rowbase = __builtin_amdgcn_readfirstlane(ti.rowbase);
-  return ti;
-}
-
 // One K stage of one wave: its four 16-row weight tiles against its first JN 16-token tiles (the tiles of
 // its 128 tokens that hold rows of the M tile, rounded up to an even count; the others are neither read
 // nor multiplied). E4M3: every 16x16x128 product is a fresh partial sum, scaled by (token scale x weight
@@ -231,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
   int ktile = 0;                           // tiles the loader has started, minus one
   auto next_id = [&](int k) { return __builtin_amdgcn_readfirstlane(ids[k & 3]); };
   const int nt_s = max(1, GATEUP ? a.fs / 128 : a.d / kBW);
-  auto decode = [&](int id) { return decode_tile_lds(id, mtp, goff, E, a.T, nt_r, nt_s); };
+  auto decode = [&](int id) { return decode_tile_lds<kBM>(id, mtp, goff, E, a.T, nt_r, nt_s); };
 
   // ---- loader geometry. Thread tid moves, per stage and operand, chunks id = 512 q + tid (q < 4): LDS
   // row id / 8 = 64 q + lrow, LDS position id % 8, which holds global chunk (id % 8) ^ (row & 7).
