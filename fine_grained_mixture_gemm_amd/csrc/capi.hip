@@ -448,12 +448,9 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   if (xsb) {
     const int kblk = c->d_model / 128;
     MOE_TRY(hip_status(launch_scales_by_block(xs, kblk, perm, offsets + c->n_routed, (int)rows,
-                                              reinterpret_cast<float*>(base + L.xsb_r), (int)rows, s),
+                                              reinterpret_cast<float*>(base + L.xsb_r), (int)rows, fs > 0 ? c->T : 0,
+                                              reinterpret_cast<float*>(base + L.xsb_s), c->T, s),
                        "scale layout launch"));
-    if (fs > 0)
-      MOE_TRY(hip_status(launch_scales_by_block(xs, kblk, nullptr, nullptr, c->T, reinterpret_cast<float*>(base + L.xsb_s),
-                                                c->T, s),
-                         "scale layout launch"));
   }
   mark(MOE_MARK_QUANT_END, s);
   // gate/up + SwiGLU

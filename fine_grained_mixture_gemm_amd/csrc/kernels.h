@@ -129,8 +129,9 @@ int dispatch_chunks(int T);
 hipError_t launch_quant_act(const void* x, bool x_bf16, int rows, int cols, uint8_t* q, float* scales, hipStream_t s);
 // out[kb * ld + r] = xs[src(r) * kblk + kb] for r < n, src(r) = perm[r] (perm non-null; n = *n_rows, the
 // dispatched row count, at most rows) or r (perm null; n = rows): the 1x128 scales of gathered rows, block-major.
+// The same launch also writes out2[kb * ld2 + r] = xs[r * kblk + kb] for r < rows2 (rows2 = 0: nothing).
 hipError_t launch_scales_by_block(const float* xs, int kblk, const int32_t* perm, const int32_t* n_rows, int rows,
-                                  float* out, int ld, hipStream_t s);
+                                  float* out, int ld, int rows2, float* out2, int ld2, hipStream_t s);
 hipError_t launch_quant_weight(const float* w, int batch, int rows, int cols, uint8_t* q, float* scales, hipStream_t s);
 hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_prefix, hipStream_t s);
 // M-tile prefix plus, for the gate/up (k = 0) and down (k = 1) launches of the matrix-core GEMM, the

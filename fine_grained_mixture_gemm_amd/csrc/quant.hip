@@ -84,16 +84,26 @@ __global__ __launch_bounds__(256) void quant_weight_128x128(const float* __restr
 }
 
 // 64 rows per block: their scales are read row by row (contiguous) into LDS and written block by block.
-__global__ __launch_bounds__(256) void scales_by_block(const float* __restrict__ xs, int kblk,
-                                                       const int32_t* __restrict__ perm, const int32_t* __restrict__ n_rows,
-                                                       int rows, float* __restrict__ out, int ld) {
+// One launch does up to two copies: blocks below nb1 the first (gathered through perm), the rest the second.
+struct ScaleCopy {
+  const int32_t* perm;
+  const int32_t* n_rows;
+  int rows;
+  float* out;
+  int ld;
+};
+
+__global__ __launch_bounds__(256) void scales_by_block(const float* __restrict__ xs, int kblk, ScaleCopy c1, int nb1,
+                                                       ScaleCopy c2) {
   __shared__ float tile[64][65];
   __shared__ int src[64];
-  const int r0 = blockIdx.x * 64;
-  const int n = perm ? min(*n_rows, rows) : rows;
+  const bool first = (int)blockIdx.x < nb1;
+  const ScaleCopy& c = first ? c1 : c2;
+  const int r0 = (first ? blockIdx.x : blockIdx.x - nb1) * 64;
+  const int n = c.perm ? min(*c.n_rows, c.rows) : c.rows;
   if (r0 >= n) return;
   const int nr = min(64, n - r0);
-  if (threadIdx.x < nr) src[threadIdx.x] = perm ? perm[r0 + threadIdx.x] : r0 + threadIdx.x;
+  if (threadIdx.x < nr) src[threadIdx.x] = c.perm ? c.perm[r0 + threadIdx.x] : r0 + threadIdx.x;
   __syncthreads();
   for (int kb0 = 0; kb0 < kblk; kb0 += 64) {
     const int kc = min(64, kblk - kb0);
@@ -104,16 +114,18 @@ __global__ __launch_bounds__(256) void scales_by_block(const float* __restrict__
     __syncthreads();
     for (int i = threadIdx.x; i < 64 * kc; i += 256) {
       const int kb = i >> 6, rr = i & 63;
-      if (rr < nr) out[(size_t)(kb0 + kb) * ld + r0 + rr] = tile[rr][kb];
+      if (rr < nr) c.out[(size_t)(kb0 + kb) * c.ld + r0 + rr] = tile[rr][kb];
     }
     __syncthreads();
   }
 }
 
 hipError_t launch_scales_by_block(const float* xs, int kblk, const int32_t* perm, const int32_t* n_rows, int rows,
-                                  float* out, int ld, hipStream_t s) {
-  if (rows == 0 || kblk == 0) return hipSuccess;
-  scales_by_block<<<(rows + 63) / 64, 256, 0, s>>>(xs, kblk, perm, n_rows, rows, out, ld);
+                                  float* out, int ld, int rows2, float* out2, int ld2, hipStream_t s) {
+  if (kblk == 0 || rows + rows2 == 0) return hipSuccess;
+  const int nb1 = (rows + 63) / 64, nb2 = (rows2 + 63) / 64;
+  scales_by_block<<<nb1 + nb2, 256, 0, s>>>(xs, kblk, ScaleCopy{perm, n_rows, rows, out, ld}, nb1,
+                                            ScaleCopy{nullptr, nullptr, rows2, out2, ld2});
   return hipGetLastError();
 }
 

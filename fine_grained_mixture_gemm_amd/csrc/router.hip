@@ -487,8 +487,9 @@ __global__ __launch_bounds__(256) void router_topk(const float* __restrict__ z, 
 }
 
 // ------------------------------------------------------------------ fp64 recheck of close tokens
-// Pass 1: fp64 logits of the flagged tokens. One block per routed expert e holds centroid row e in
-// registers (each thread every 256th element, as fp64) and takes the flagged tokens 8 at a time, reading
+// Pass 1: fp64 logits of the flagged tokens. Eight blocks per routed expert e hold centroid row e in
+// registers (each thread every 256th element, as fp64); block y takes batches y, y + 8, ... of 8 flagged
+// tokens (so a handful of flagged tokens does not run as one long chain of batches per expert), reading
 // their u elements straight from memory (every element is used once per block, so there is nothing to
 // stage; the flagged rows stay in L2 for the other blocks); each of the 8 dot products is reduced in
 // fp64. Products of the stored inputs are exact in fp64.
@@ -496,6 +497,7 @@ constexpr int kRecheckThreads = 256;
 constexpr int kRecheckMaxD = 8192;
 constexpr int kRecheckPer = kRecheckMaxD / kRecheckThreads;   // centroid elements per thread (32)
 constexpr int kRecheckBatch = 8;                               // flagged tokens per pass
+constexpr int kRecheckSplit = 8;                               // blocks per expert, each every 8th batch
 
 template <typename TU>
 __global__ __launch_bounds__(kRecheckThreads) void router_recheck_logits(const TU* __restrict__ u,
@@ -506,7 +508,8 @@ __global__ __launch_bounds__(kRecheckThreads) void router_recheck_logits(const T
                                                                          double* __restrict__ z64) {
   __shared__ double part[kRecheckBatch][kRecheckThreads / 64];
   const int n = *recheck_count;
-  if (n == 0) return;
+  // blockIdx.y takes batches y, y + gridDim.y, ... of the flagged tokens
+  if (n <= (int)blockIdx.y * kRecheckBatch) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = blockIdx.x; e < E; e += gridDim.x) {
     // indices past d are clamped (no branches, so every load can be in flight at once); their centroid
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(kRecheckThreads) void router_recheck_logits(const T
       w[i] = k < d ? v : 0.0;
     }
     const double o = off ? (double)off[e] : 0.0;
-    for (int q0 = 0; q0 < n; q0 += kRecheckBatch) {
+    for (int q0 = blockIdx.y * kRecheckBatch; q0 < n; q0 += gridDim.y * kRecheckBatch) {
       const int nb = min(kRecheckBatch, n - q0);
       double acc[kRecheckBatch];
 #pragma unroll
@@ -688,10 +691,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
                                                            a.topk_groups, a.delta, a.d, a.un2, nsl, a.wn2, a.topk_idx,
                                                            a.topk_w, a.recheck_count, a.recheck_list);
   if (a.u_bf16)
-    router_recheck_logits<uint16_t><<<a.E, kRecheckThreads, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.E, a.d,
+    router_recheck_logits<uint16_t><<<dim3(a.E, kRecheckSplit), kRecheckThreads, 0, s>>>((const uint16_t*)a.u, a.wg, a.off, a.E, a.d,
                                                                      a.recheck_count, a.recheck_list, a.z64);
   else
-    router_recheck_logits<float><<<a.E, kRecheckThreads, 0, s>>>((const float*)a.u, a.wg, a.off, a.E, a.d,
+    router_recheck_logits<float><<<dim3(a.E, kRecheckSplit), kRecheckThreads, 0, s>>>((const float*)a.u, a.wg, a.off, a.E, a.d,
                                                                   a.recheck_count, a.recheck_list, a.z64);
   if (a.gate == MOE_GATE_SOFTMAX)
     router_recheck_select<MOE_GATE_SOFTMAX><<<64, 256, 0, s>>>(a.z64, a.E, a.K, a.bias, a.renorm, a.n_groups,
