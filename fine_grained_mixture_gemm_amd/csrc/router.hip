@@ -119,11 +119,25 @@ __global__ __launch_bounds__(256) void router_prep_wg(const float* __restrict__ 
   const int e = blockIdx.x;
   const size_t n = (size_t)E * d;
   float s = 0.f;
-  for (int k = threadIdx.x; k < d; k += 256) {
-    const size_t i = (size_t)e * d + k;
-    const float v = wg[i];
-    s = fmaf(v, v, s);
-    if constexpr (SPLIT) split_bf16x3(v, parts[i], parts[n + i], parts[2 * n + i]);
+  // each thread's elements k = tid, tid + 256, ... in groups of 16, all loads of a group in flight at once;
+  // the squares are added in k order either way
+  constexpr int kG = 16;
+  for (int k0 = threadIdx.x; k0 < d; k0 += 256 * kG) {
+    float v[kG];
+#pragma unroll
+    for (int q = 0; q < kG; ++q) {
+      const int k = k0 + 256 * q;
+      v[q] = k < d ? wg[(size_t)e * d + k] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < kG; ++q) {
+      const int k = k0 + 256 * q;
+      if (k < d) {
+        const size_t i = (size_t)e * d + k;
+        s = fmaf(v[q], v[q], s);
+        if constexpr (SPLIT) split_bf16x3(v[q], parts[i], parts[n + i], parts[2 * n + i]);
+      }
+    }
   }
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;

@@ -23,6 +23,8 @@ SMALL = {
     # other way moves a row of y by about 0.3 * 3 / sqrt(f) of its RMS, so small f inflates the error.
     "fp8_sigmoid_ragged": W["v3_fp8"].replace(name="fp8_sigmoid_ragged", T=333, d=512, E=20, K=4),
     "fp8_k_equals_e": W["v3_fp8"].replace(name="fp8_k_equals_e", T=70, d=256, E=4, K=4),
+    # no shared experts on the tiled E4M3 path (its scale copy then has no shared part)
+    "fp8_no_shared": W["v3_fp8"].replace(name="fp8_no_shared", T=260, d=512, E=16, Ks=0, K=4),
     "fp8_one_token": W["v3_fp8"].replace(name="fp8_one_token", T=1, d=256, E=32, K=8),
     # batches of at most 128 tokens take the E4M3 decode kernels: groups spanning 3 and 4 token tiles,
     # two shared experts (shared inner dim 2 f)
