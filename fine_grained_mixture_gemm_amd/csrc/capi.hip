@@ -3,8 +3,10 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <mutex>
 #include <string>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -321,6 +323,15 @@ moe_status weight_gradients(const moe_config* c, const BwdLayout& L, uint8_t* ba
   return MOE_OK;
 }
 
+// The kernels read and write activations, expert weights and expert outputs in 16-byte pieces: each
+// such buffer (when given) must start on a 16-byte boundary.
+moe_status check_aligned16(std::initializer_list<std::pair<const char*, const void*>> bufs) {
+  for (const auto& b : bufs)
+    if (b.second && (reinterpret_cast<uintptr_t>(b.second) & 15))
+      return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", b.first);
+  return MOE_OK;
+}
+
 moe_status check_layer_router(const moe_layer* l) {
   if (!l) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
   if (!l->w_gate) return fail(MOE_ERR_INVALID_ARG, "layer->w_gate is NULL");
@@ -340,7 +351,7 @@ moe_status check_layer_experts(const moe_config* c, const moe_layer* l) {
     if (!l->ws13 || !l->ws2) return fail(MOE_ERR_INVALID_ARG, "n_shared > 0 needs ws13 and ws2");
     if (fp8 && (!l->ws13_scale || !l->ws2_scale)) return fail(MOE_ERR_INVALID_ARG, "fp8 shared weights need scales");
   }
-  return MOE_OK;
+  return check_aligned16({{"layer->w13", l->w13}, {"layer->w2", l->w2}, {"layer->ws13", l->ws13}, {"layer->ws2", l->ws2}});
 }
 
 RouteArgs route_args(const moe_config* c, const moe_layer* l, const void* u, const float* bias, int32_t* idx, float* w,
@@ -546,6 +557,7 @@ moe_status moe_route(const moe_config* cfg, const moe_layer* layer, const void* 
   MOE_TRY(check_cfg(cfg));
   MOE_TRY(check_layer_router(layer));
   if (cfg->T > 0 && (!u || !topk_idx || !topk_w)) return fail(MOE_ERR_INVALID_ARG, "u / topk_idx / topk_w is NULL");
+  MOE_TRY(check_aligned16({{"u", u}}));
   uint8_t* base;
   Layout L;
   MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
@@ -558,6 +570,7 @@ moe_status moe_router_logits(const moe_config* cfg, const moe_layer* layer, cons
   MOE_TRY(check_cfg(cfg));
   MOE_TRY(check_layer_router(layer));
   if (cfg->T > 0 && (!u || !z)) return fail(MOE_ERR_INVALID_ARG, "u / z is NULL");
+  MOE_TRY(check_aligned16({{"u", u}}));
   uint8_t* base;
   Layout L;
   MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
@@ -588,6 +601,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, const moe_layer* layer, const v
   MOE_TRY(check_layer_experts(cfg, layer));
   if (cfg->T > 0 && (!u || !offsets || !perm_src || !y_routed)) return fail(MOE_ERR_INVALID_ARG, "u / offsets / perm_src / y_routed is NULL");
   if (cfg->T > 0 && cfg->n_shared > 0 && !y_shared) return fail(MOE_ERR_INVALID_ARG, "y_shared is NULL with n_shared > 0");
+  MOE_TRY(check_aligned16({{"u", u}, {"y_routed", y_routed}, {"y_shared", cfg->n_shared > 0 ? y_shared : nullptr}}));
   uint8_t* base;
   Layout L;
   MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
@@ -600,6 +614,7 @@ moe_status moe_combine(const moe_config* cfg, const void* u, const void* y_route
   if (cfg->T == 0) return MOE_OK;
   if (!u || !y_routed || !row_of || !topk_w || !h) return fail(MOE_ERR_INVALID_ARG, "combine pointer is NULL");
   if (cfg->n_shared > 0 && !y_shared) return fail(MOE_ERR_INVALID_ARG, "y_shared is NULL with n_shared > 0");
+  MOE_TRY(check_aligned16({{"u", u}, {"y_routed", y_routed}, {"y_shared", cfg->n_shared > 0 ? y_shared : nullptr}, {"h", h}}));
   const bool bf16 = cfg->act_dtype == MOE_BF16;
   MOE_TRY(hip_status(launch_combine(u, bf16, y_routed, cfg->n_shared > 0 ? y_shared : nullptr, esz_y(cfg) == 2, row_of,
                                     topk_w, cfg->T, cfg->d_model, cfg->top_k, h, stream),
@@ -614,6 +629,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_layer* layer, const void
   MOE_TRY(check_layer_router(layer));
   MOE_TRY(check_layer_experts(cfg, layer));
   if (cfg->T > 0 && (!u || !h)) return fail(MOE_ERR_INVALID_ARG, "u / h is NULL");
+  MOE_TRY(check_aligned16({{"u", u}, {"h", h}}));
   uint8_t* base;
   Layout L;
   MOE_TRY(check_ws(cfg, ws, ws_bytes, &base, &L));
@@ -750,6 +766,7 @@ moe_status moe_pack_weights(const moe_config* cfg, int32_t which, const void* sr
   if (rows % 256) return fail(MOE_ERR_UNSUPPORTED, "the matrix has %d rows, not a multiple of 256", rows);
   if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "src / dst is NULL");
   if (src == dst) return fail(MOE_ERR_INVALID_ARG, "the layout change cannot run in place");
+  MOE_TRY(check_aligned16({{"src", src}, {"dst", dst}}));
   // check_cfg has d % 256 == 0 and f % 128 == 0: gate/up tiles of 128 + 128 rows, down tiles of 256 rows,
   // 128-byte K stages
   return hip_status(launch_pack_weights(src, dst, groups, rows, cols * esz, gateup, stream), "weight layout launch");
@@ -761,6 +778,7 @@ moe_status moe_transpose_fp8_weights(const uint8_t* q, const float* scales, int3
   if (rows % 128 || cols % 128) return fail(MOE_ERR_UNSUPPORTED, "rows and cols must be multiples of 128");
   if (batch > 65535 || rows / 64 > 65535) return fail(MOE_ERR_UNSUPPORTED, "too many blocks");
   if (batch > 0 && (!q || !scales || !qt || !scales_t)) return fail(MOE_ERR_INVALID_ARG, "q / scales / qt / scales_t is NULL");
+  MOE_TRY(check_aligned16({{"q", q}, {"qt", qt}}));
   return hip_status(launch_transpose_fp8(q, scales, batch, rows, cols, qt, scales_t, stream), "weight transpose launch");
 }
 
@@ -781,6 +799,9 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, const moe_layer* layer
     return fail(MOE_ERR_INVALID_ARG, "u / offsets / perm_src / dy_routed is NULL");
   if (c->T > 0 && sh && !dy_shared) return fail(MOE_ERR_INVALID_ARG, "dy_shared is NULL with n_shared > 0");
   if (want_dx && c->T > 0 && sh && !dx_shared) return fail(MOE_ERR_INVALID_ARG, "dx_shared is NULL with n_shared > 0");
+  MOE_TRY(check_aligned16({{"u", u}, {"dy_routed", dy_routed}, {"dy_shared", sh ? dy_shared : nullptr},
+                           {"dx_routed", dx_routed}, {"dx_shared", sh ? dx_shared : nullptr}, {"dw13", dw13},
+                           {"dw2", dw2}, {"dws13", sh ? dws13 : nullptr}, {"dws2", sh ? dws2 : nullptr}}));
   const BwdLayout L = bwd_layout(c);
   if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
@@ -902,6 +923,7 @@ moe_status moe_quantize_weights(const float* w, int32_t batch, int32_t rows, int
   if (rows % 128 || cols % 128) return fail(MOE_ERR_UNSUPPORTED, "rows and cols must be multiples of 128");
   if (batch > 65535 || rows / 128 > 65535) return fail(MOE_ERR_UNSUPPORTED, "too many blocks");
   if (batch > 0 && (!w || !q || !scales)) return fail(MOE_ERR_INVALID_ARG, "w / q / scales is NULL");
+  MOE_TRY(check_aligned16({{"w", w}, {"q", q}}));
   return hip_status(launch_quant_weight(w, batch, rows, cols, q, scales, stream), "weight quantization launch");
 }
 
@@ -911,6 +933,7 @@ moe_status moe_quantize_act(const void* x, int32_t x_dtype, int32_t rows, int32_
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "x_dtype must be F32 or BF16");
   if (cols % 128) return fail(MOE_ERR_UNSUPPORTED, "cols must be a multiple of 128");
   if (rows > 0 && (!x || !q || !scales)) return fail(MOE_ERR_INVALID_ARG, "x / q / scales is NULL");
+  MOE_TRY(check_aligned16({{"x", x}, {"q", q}}));
   return hip_status(launch_quant_act(x, x_dtype == MOE_BF16, rows, cols, q, scales, stream), "activation quantization launch");
 }
 

@@ -17,6 +17,9 @@
  *  - Every pointer argument is a DEVICE pointer unless marked "host". The caller owns every buffer;
  *    the library allocates nothing. Scratch memory comes from a caller-provided workspace of at least
  *    moe_workspace_size() bytes, 256-byte aligned.
+ *  - Device buffers of activations, weights, expert outputs and gradients must start on a 16-byte
+ *    boundary (the kernels move them in 16-byte pieces); a misaligned one fails with
+ *    MOE_ERR_INVALID_ARG. torch and hipMalloc allocations always satisfy this.
  *  - Calls validate their arguments synchronously (nothing is launched when they fail) and then enqueue
  *    work on `stream` asynchronously. They never abort and never synchronize the device.
  *  - Matrices are row-major. T = tokens, d = d_model, E = routed experts, Ks = shared experts,

@@ -206,3 +206,31 @@ def test_weight_layout_argument_errors():
     assert lib.moe_expert_ffn(ctypes.byref(cfg), ctypes.byref(bad), 16, 16, 16, 16, 16, 16, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     tiled32 = moe.moe_layer(16, 16, None, None, 16, 16, None, None, 16, None, moe.MOE_LAYOUT_TILED)
     assert lib.moe_expert_ffn(ctypes.byref(f32), ctypes.byref(tiled32), 16, 16, 16, 16, 16, 16, 1 << 30, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_misaligned_buffers_are_rejected():
+    # the kernels move activations, weights and expert outputs in 16-byte pieces: an address off a 16-byte
+    # boundary fails validation (the dummy addresses are never dereferenced)
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    P = ctypes.POINTER
+    cfg = _cfg()
+    layer = moe.moe_layer()
+    layer.w_gate = 16
+    lib.moe_route.argtypes = [P(moe.moe_config), P(moe.moe_layer)] + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert lib.moe_route(ctypes.byref(cfg), ctypes.byref(layer), 24, None, 16, 16, 16, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert "aligned" in moe.moe_last_error() and "u" in moe.moe_last_error()
+    lib.moe_expert_ffn.argtypes = [P(moe.moe_config), P(moe.moe_layer)] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]
+    layer.w13, layer.w2, layer.w13_scale, layer.w2_scale = 16, 16, 16, 16
+    layer.ws13, layer.ws2, layer.ws13_scale, layer.ws2_scale = 16, 16, 16, 16
+    ffn = lambda u=16, yr=16, ys=16: lib.moe_expert_ffn(ctypes.byref(cfg), ctypes.byref(layer), u, 16, 16, yr, ys, 16,
+                                                        1 << 30, None)
+    assert ffn(yr=40) == moe.MOE_ERR_INVALID_ARG and "y_routed" in moe.moe_last_error()
+    assert ffn(ys=8) == moe.MOE_ERR_INVALID_ARG and "y_shared" in moe.moe_last_error()
+    layer.w2 = 48 + 4
+    assert ffn() == moe.MOE_ERR_INVALID_ARG and "layer->w2" in moe.moe_last_error()
+    layer.w2 = 16
+    lib.moe_quantize_act.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.moe_quantize_act(18, moe.MOE_BF16, 4, 128, 16, 16, None) == moe.MOE_ERR_INVALID_ARG
+    lib.moe_pack_weights.argtypes = [P(moe.moe_config), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.moe_pack_weights(ctypes.byref(cfg), moe.MOE_PACK_W2, 16, 33, None) == moe.MOE_ERR_INVALID_ARG
+    assert "dst" in moe.moe_last_error()
