@@ -2,8 +2,8 @@
 //   h_t = u_t + y_shared_t + sum_k g_{t,k} * y[row_of(t,k)]
 // summed in fp32 in that order (k ascending = expert ascending), rounded once to the output dtype.
 // A pair that dispatch dropped (row_of = -1: no routed expert, or a repeated one) adds nothing.
-// One 256-thread block per token; each thread reads and writes 16-byte pieces of the rows, so every
-// row access is a contiguous, coalesced sweep.
+// One block per token (d/16 threads rounded up to whole waves, 64 to 1024); each thread reads and writes
+// 16-byte pieces of the rows, so every row access is a contiguous, coalesced sweep.
 //
 // Bias update (same report, 3.3): b_i - gamma for an overloaded expert, b_i + gamma for an
 // underloaded one, unchanged at the mean load; decided in integers as counts_i * E against T * K.
@@ -18,7 +18,7 @@ constexpr int kCombineMaxK = 8;   // routed rows held in registers at once (bf16
 
 // BF16: u and h are bf16 (else fp32); YBF16: the expert outputs are bf16 (else fp32).
 template <bool BF16, bool YBF16>
-__global__ __launch_bounds__(256) void combine_rows(const void* __restrict__ u_, const void* __restrict__ yr_,
+__global__ __launch_bounds__(1024) void combine_rows(const void* __restrict__ u_, const void* __restrict__ yr_,
                                                     const void* __restrict__ ys_, const int32_t* __restrict__ row_of,
                                                     const float* __restrict__ topk_w, int d, int K,
                                                     void* __restrict__ h_) {
@@ -116,9 +116,11 @@ __global__ __launch_bounds__(256) void combine_rows(const void* __restrict__ u_,
 hipError_t launch_combine(const void* u, bool bf16, const void* y_routed, const void* y_shared, bool y_bf16,
                           const int32_t* row_of, const float* topk_w, int T, int d, int K, void* h, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (bf16 && y_bf16) combine_rows<true, true><<<T, 256, 0, s>>>(u, y_routed, y_shared, row_of, topk_w, d, K, h);
-  else if (bf16) combine_rows<true, false><<<T, 256, 0, s>>>(u, y_routed, y_shared, row_of, topk_w, d, K, h);
-  else if (!y_bf16) combine_rows<false, false><<<T, 256, 0, s>>>(u, y_routed, y_shared, row_of, topk_w, d, K, h);
+  // about two 8-element pieces of the row per thread, so that few threads run a third round
+  const int nt = std::min(1024, std::max(64, ((d / 8 + 1) / 2 + 63) / 64 * 64));
+  if (bf16 && y_bf16) combine_rows<true, true><<<T, nt, 0, s>>>(u, y_routed, y_shared, row_of, topk_w, d, K, h);
+  else if (bf16) combine_rows<true, false><<<T, nt, 0, s>>>(u, y_routed, y_shared, row_of, topk_w, d, K, h);
+  else if (!y_bf16) combine_rows<false, false><<<T, nt, 0, s>>>(u, y_routed, y_shared, row_of, topk_w, d, K, h);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

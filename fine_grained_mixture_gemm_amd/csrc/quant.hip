@@ -7,42 +7,48 @@
 
 namespace moe {
 
-// 16 lanes per 128-column group, 8 consecutive elements per lane; one 256-thread block covers
-// 16 groups (2048 columns of one row, or several rows when cols is smaller).
+// 8 lanes per 128-column group, 16 consecutive elements (one or more 16-byte loads, one 16-byte store)
+// per lane; one 256-thread block covers 32 groups (4096 columns of one row, or several rows when cols is
+// smaller).
 template <typename TX>
 __global__ __launch_bounds__(256) void quant_act_1x128(const TX* __restrict__ x, int rows, int cols,
                                                        uint8_t* __restrict__ q, float* __restrict__ scales) {
   const int groups_per_row = cols / 128;
-  const long long group = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  if (group >= (long long)rows * groups_per_row) return;   // 16-lane groups exit together
+  const long long group = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
+  if (group >= (long long)rows * groups_per_row) return;   // 8-lane groups exit together
   const int row = (int)(group / groups_per_row), gc = (int)(group % groups_per_row);
-  const int sub = threadIdx.x & 15;
-  const size_t base = (size_t)row * cols + (size_t)gc * 128 + sub * 8;
-  float v[8];
+  const int sub = threadIdx.x & 7;
+  const size_t base = (size_t)row * cols + (size_t)gc * 128 + sub * 16;
+  float v[16];
   if constexpr (sizeof(TX) == 2) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(x + base);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const uint4 r0 = *reinterpret_cast<const uint4*>(x + base);
+    const uint4 r1 = *reinterpret_cast<const uint4*>(x + base + 8);
+    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       v[2 * i] = __uint_as_float(w[i] << 16);
       v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   } else {
-    const float4 a = *reinterpret_cast<const float4*>(x + base);
-    const float4 b = *reinterpret_cast<const float4*>(x + base + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 a = *reinterpret_cast<const float4*>(x + base + 4 * i);
+      v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+    }
   }
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
-  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  for (int o = 4; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
   float s, inv;
   e4m3_scales(amax, s, inv);
-  uint2 out;
+  uint4 out;
   out.x = f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
   out.y = f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-  *reinterpret_cast<uint2*>(q + base) = out;
+  out.z = f32x4_to_e4m3x4(v[8] * inv, v[9] * inv, v[10] * inv, v[11] * inv);
+  out.w = f32x4_to_e4m3x4(v[12] * inv, v[13] * inv, v[14] * inv, v[15] * inv);
+  *reinterpret_cast<uint4*>(q + base) = out;
   if (sub == 0) scales[(size_t)row * groups_per_row + gc] = s;
 }
 
@@ -132,7 +138,7 @@ hipError_t launch_scales_by_block(const float* xs, int kblk, const int32_t* perm
 hipError_t launch_quant_act(const void* x, bool x_bf16, int rows, int cols, uint8_t* q, float* scales, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const long long groups = (long long)rows * (cols / 128);
-  const unsigned nb = (unsigned)((groups + 15) / 16);
+  const unsigned nb = (unsigned)((groups + 31) / 32);
   if (x_bf16) quant_act_1x128<uint16_t><<<nb, 256, 0, s>>>((const uint16_t*)x, rows, cols, q, scales);
   else quant_act_1x128<float><<<nb, 256, 0, s>>>((const float*)x, rows, cols, q, scales);
   return hipGetLastError();
