@@ -108,7 +108,7 @@ moe_status check_cfg(const moe_config* c) {
 
 struct Layout {
   size_t z, z64, wg_split, zpart, recheck_count, recheck_list, wn2, un2;
-  size_t chunk_counts, chunk_base, mt_prefix, xsched;
+  size_t chunk_counts, mt_prefix, xsched;
   size_t uq, us, xsb_r, xsb_s, a_r, a_s, as_r, as_s;
   size_t f_idx, f_w, f_counts, f_offsets, f_perm, f_rowof, f_yr, f_ys;
   size_t bal_psum, bal_cnt, bal_seqp, bal_seqn, bal_seq;
@@ -140,7 +140,6 @@ Layout layout(const moe_config* c) {
   L.un2 = take((use_mfma_router(c) ? 4 : (size_t)ksplit) * T * 4);   // token norms per slice of d
   const size_t nch = dispatch_chunks(c->T);
   L.chunk_counts = take(nch * E * 4);
-  L.chunk_base = take(nch * E * 4);
   L.mt_prefix = take((E + 1) * 4);
   L.xsched = take(2 * (kSchedRange + kSchedCount) * 4);
   L.uq = take(fp8 ? T * d : 0);
@@ -403,7 +402,6 @@ moe_status do_dispatch(const moe_config* c, const int32_t* idx, int32_t* counts,
   a.E = c->n_routed;
   a.K = c->top_k;
   a.chunk_counts = reinterpret_cast<int32_t*>(base + L.chunk_counts);
-  a.chunk_base = reinterpret_cast<int32_t*>(base + L.chunk_base);
   a.counts = counts;
   a.offsets = offsets;
   a.perm_src = perm;

@@ -99,34 +99,36 @@ __global__ __launch_bounds__(kChunk) void dispatch_count(const int32_t* __restri
   }
 }
 
-// One block: per-expert running sums over chunks, expert counts and offsets.
-__global__ __launch_bounds__(256) void dispatch_scan(const int32_t* __restrict__ chunk_counts, int nchunks, int E,
-                                                     int32_t* __restrict__ chunk_base, int32_t* __restrict__ counts,
-                                                     int32_t* __restrict__ offsets) {
-  __shared__ int s_wave[kChunk / 64];
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      chunk_base[(size_t)c * E + e] = run;
-      run += chunk_counts[(size_t)c * E + e];
-    }
-    counts[e] = run;
-  }
-  int total;
-  const int off = block_exclusive_scan_256(e < E ? run : 0, s_wave, total);
-  if (e < E) offsets[e] = off;
-  if (e == 0) offsets[E] = total;
-}
-
+// Every block first reads all chunks' counts (E x chunks values, from L2): thread e sums expert e's
+// counts over the chunks before this one (its rows come after theirs) and over all chunks (the expert's
+// count), and a block-wide scan of the counts gives the experts' first rows. Block 0 also writes counts
+// and offsets. This replaces a separate scan launch between the two passes.
 __global__ __launch_bounds__(kChunk) void dispatch_scatter(const int32_t* __restrict__ idx, int T, int E, int K,
-                                                           const int32_t* __restrict__ chunk_base,
-                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ chunk_counts, int nchunks,
+                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm_src, int32_t* __restrict__ row_of) {
   __shared__ uint32_t bits[256][kWords];
   __shared__ int32_t base[256];
-  const int c = blockIdx.x, t = c * kChunk + threadIdx.x;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) base[e] = offsets[e] + chunk_base[(size_t)c * E + e];
+  __shared__ int s_wave[kChunk / 64];
+  const int c = blockIdx.x, t = c * kChunk + threadIdx.x, e = threadIdx.x;
+  int before = 0, total_e = 0;
+  if (e < E) {
+    for (int cc = 0; cc < nchunks; ++cc) {
+      const int v = chunk_counts[(size_t)cc * E + e];
+      before += cc < c ? v : 0;
+      total_e += v;
+    }
+  }
+  int total;
+  const int off = block_exclusive_scan_256(e < E ? total_e : 0, s_wave, total);
+  if (e < E) {
+    base[e] = off + before;
+    if (c == 0) {
+      counts[e] = total_e;
+      offsets[e] = off;
+    }
+  }
+  if (c == 0 && e == 0) offsets[E] = total;
   int ids[16];
   load_ids(idx, t, T, K, ids);
   build_bits(bits, ids, t, T, E, K);   // its barriers also publish `base`
@@ -169,8 +171,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   }
   const int nchunks = cdiv(a.T, kChunk);
   dispatch_count<<<nchunks, kChunk, 0, s>>>(a.topk_idx, a.T, a.E, a.K, a.chunk_counts);
-  dispatch_scan<<<1, 256, 0, s>>>(a.chunk_counts, nchunks, a.E, a.chunk_base, a.counts, a.offsets);
-  dispatch_scatter<<<nchunks, kChunk, 0, s>>>(a.topk_idx, a.T, a.E, a.K, a.chunk_base, a.offsets, a.perm_src, a.row_of);
+  dispatch_scatter<<<nchunks, kChunk, 0, s>>>(a.topk_idx, a.T, a.E, a.K, a.chunk_counts, nchunks, a.counts, a.offsets,
+                                              a.perm_src, a.row_of);
   return hipGetLastError();
 }
 

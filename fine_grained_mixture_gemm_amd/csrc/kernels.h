@@ -71,7 +71,6 @@ struct DispatchArgs {
   const int32_t* topk_idx;
   int T, E, K;
   int32_t* chunk_counts;  // [chunks, E]
-  int32_t* chunk_base;    // [chunks, E]
   int32_t* counts;
   int32_t* offsets;
   int32_t* perm_src;
