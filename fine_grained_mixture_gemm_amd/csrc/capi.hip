@@ -334,7 +334,7 @@ moe_status check_aligned16(std::initializer_list<std::pair<const char*, const vo
 moe_status check_layer_router(const moe_layer* l) {
   if (!l) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
   if (!l->w_gate) return fail(MOE_ERR_INVALID_ARG, "layer->w_gate is NULL");
-  return MOE_OK;
+  return check_aligned16({{"layer->w_gate", l->w_gate}});
 }
 
 moe_status check_layer_experts(const moe_config* c, const moe_layer* l) {
@@ -423,9 +423,12 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   const int fs = c->n_shared * c->inter_dim;
   // a decode-sized E4M3 batch streams the touched experts' weights with its own kernels (no tile list)
   const bool decode = fp8 && c->T <= gemm_decode_max_tokens();
-  if (mfma && !decode) {
-    const int nt_r[2] = {c->inter_dim / 128, c->d_model / 256}, nt_s[2] = {fs / 128, fs > 0 ? c->d_model / 256 : 0};
-    MOE_TRY(hip_status(launch_schedule_mfma(offsets, c->n_routed, c->T, bm, nt_r, nt_s, mt_prefix, xrange, xcount, s),
+  // E4M3 on the matrix-core tiles: the schedule is computed by the activation quantization's launch
+  const bool fused = fp8 && mfma && !decode;
+  SchedArgs sa{offsets, c->n_routed, c->T, bm, {c->inter_dim / 128, c->d_model / 256},
+               {fs / 128, fs > 0 ? c->d_model / 256 : 0}, mt_prefix, xrange, xcount};
+  if (mfma && !decode && !fused) {
+    MOE_TRY(hip_status(launch_schedule_mfma(offsets, c->n_routed, c->T, bm, sa.nt_r, sa.nt_s, mt_prefix, xrange, xcount, s),
                        "schedule launch"));
   } else if (!mfma) {
     MOE_TRY(hip_status(launch_schedule(offsets, c->n_routed, bm, mt_prefix, s), "schedule launch"));
@@ -444,7 +447,12 @@ moe_status do_ffn(const moe_config* c, const moe_layer* l, const void* u, const 
   g.packed = l->weight_layout == MOE_LAYOUT_TILED;
   const uint8_t* xin = static_cast<const uint8_t*>(u);
   const float* xs = nullptr;
-  if (fp8) {
+  if (fused) {
+    MOE_TRY(hip_status(launch_quant_act_schedule(u, c->T, c->d_model, base + L.uq, reinterpret_cast<float*>(base + L.us), sa, s),
+                       "activation quantization and schedule launch"));
+    xin = base + L.uq;
+    xs = reinterpret_cast<const float*>(base + L.us);
+  } else if (fp8) {
     MOE_TRY(hip_status(launch_quant_act(u, true, c->T, c->d_model, base + L.uq, reinterpret_cast<float*>(base + L.us), s),
                        "activation quantization launch"));
     xin = base + L.uq;

@@ -31,99 +31,11 @@ hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_pr
   return hipGetLastError();
 }
 
-// Schedule of the matrix-core grouped GEMMs. The tile list (routed experts ascending, M index fastest
-// within an N tile, then the shared group) is cut into eight contiguous ranges of equal estimated
-// cost, one per XCD, over the first 7/8 of the total; the rest is a pool for any XCD whose range is
-// done. A tile's cost follows its measured duration by valid rows (below): 100 when more
-// than half of its bm rows are valid (both token halves of the block multiply), 69 or 62 otherwise (one
-// half multiplies; streaming its weights still takes most of the time). Within a range the blocks of
-// that XCD take tiles in order from a counter, then from the pool's.
-// Exclusive prefix sum over the 512 threads of a block (buf: 512 entries of LDS, reusable on return):
-// a shuffle scan within each wave, then the totals of the waves before.
-__device__ __forceinline__ long long block_exclusive_scan(long long v, long long* buf) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  long long x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const long long y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) buf[wave] = x;
-  __syncthreads();
-  long long before = 0;
-  for (int w = 0; w < wave; ++w) before += buf[w];
-  __syncthreads();
-  return before + x - v;
-}
-
-// One thread per group (routed experts 0..E-1, the shared group E): its M tiles and the cost of one row
-// of N tiles, then block-wide scans give every group its first tile and the cost before it, and the
-// group holding a boundary's cost finds the boundary tile within itself.
 __global__ __launch_bounds__(512) void ffn_schedule_mfma(const int32_t* __restrict__ offsets, int E, int T, int bm,
                                                          int ntr0, int nts0, int ntr1, int nts1,
                                                          int32_t* __restrict__ mt_prefix, int32_t* __restrict__ xrange,
                                                          int32_t* __restrict__ xcount) {
-  __shared__ long long buf[512];
-  __shared__ long long s_tot[2];
-  const int g = threadIdx.x;
-  const bool grp = g <= E;
-  // relative duration of a tile by its valid rows (measured on the V3 layer, both projections: a tile
-  // whose second half of tokens is empty skips half the MFMAs, and one of at most bm/4 rows also most
-  // of the token copies; the shared group's full tiles run a little longer than routed ones)
-  auto tile_cost = [&](int n, int m) {
-    const int r = min(bm, n - m * bm);
-    return r > bm / 2 ? (g == E ? 103 : 100) : (r > bm / 4 ? 69 : 62);
-  };
-  int n = 0, mt = 0, S = 0;
-  if (grp) {
-    n = g < E ? offsets[g + 1] - offsets[g] : T;
-    mt = cdiv(n, bm);
-    for (int m = 0; m < mt; ++m) S += tile_cost(n, m);
-  }
-  if (g < 2 * kSchedCount) xcount[g] = 0;
-  // M tiles before each routed group; for g = E this is their total
-  const long long mpre = block_exclusive_scan(g < E ? mt : 0, buf);
-  if (grp) mt_prefix[g] = (int)mpre;
-  for (int l = 0; l < 2; ++l) {
-    const int nt = g < E ? (l ? ntr1 : ntr0) : (l ? nts1 : nts0);
-    const long long C = grp ? (long long)nt * S : 0;       // cost of the group's tiles
-    const long long ntl = grp ? (long long)nt * mt : 0;    // and their number
-    const long long before = block_exclusive_scan(C, buf);
-    const long long id0 = block_exclusive_scan(ntl, buf);
-    if (g == E) {
-      s_tot[0] = before + C;
-      s_tot[1] = id0 + ntl;
-    }
-    __syncthreads();
-    const long long total = s_tot[0];
-    const long long ranged = total - total / kSchedPoolDiv;   // cost of the XCD ranges; the rest is the pool
-    int32_t* r = xrange + kSchedRange * l;
-    if (g == 0) {
-      r[0] = 0;
-      r[9] = (int)s_tot[1];
-      if (ranged <= 0) r[8] = 0;
-    }
-    // boundary x: the first tile whose preceding cost reaches x * ranged / 8 (x = 8: the pool's start).
-    // The groups with tiles split (0, total] into the intervals (before, before + C]; the owner's tiles are
-    // nt equal columns of cost S (M fastest within an N column): it skips whole columns, then scans the M
-    // tiles of the next one.
-    for (int x = 1; x <= 8; ++x) {
-      const long long tgt = ranged * x / 8;
-      if (tgt <= 0) {
-        if (g == 0) r[x] = 0;
-        continue;
-      }
-      if (C > 0 && before < tgt && tgt <= before + C) {
-        const long long off = tgt - before;
-        const long long nf = off / S;        // whole N columns (each S) before the boundary
-        long long cum = nf * S;
-        int mi = 0;
-        while (cum < off) cum += tile_cost(n, mi++);
-        r[x] = (int)(id0 + nf * mt + mi);
-      }
-    }
-    __syncthreads();   // s_tot is written again by the next launch's totals
-  }
+  schedule_mfma_block(offsets, E, T, bm, ntr0, nts0, ntr1, nts1, mt_prefix, xrange, xcount);
 }
 
 hipError_t launch_schedule_mfma(const int32_t* offsets, int E, int T, int bm, const int (&nt_r)[2], const int (&nt_s)[2],

@@ -141,6 +141,18 @@ hipError_t launch_schedule(const int32_t* offsets, int E, int bm, int32_t* mt_pr
 constexpr int kSchedRange = 10, kSchedCount = 9, kSchedPoolDiv = 8;
 hipError_t launch_schedule_mfma(const int32_t* offsets, int E, int T, int bm, const int (&nt_r)[2], const int (&nt_s)[2],
                                 int32_t* mt_prefix, int32_t* xrange, int32_t* xcount, hipStream_t s);
+// The tile schedule's arguments (as launch_schedule_mfma), for launches that compute it beside other work.
+struct SchedArgs {
+  const int32_t* offsets;
+  int E, T, bm;
+  int nt_r[2], nt_s[2];
+  int32_t* mt_prefix;
+  int32_t* xrange;
+  int32_t* xcount;
+};
+// launch_quant_act (bf16 x) and launch_schedule_mfma in one launch
+hipError_t launch_quant_act_schedule(const void* x, int rows, int cols, uint8_t* q, float* scales, const SchedArgs& sa,
+                                     hipStream_t s);
 int gemm_mfma_bm();
 // raw (E4M3 only): fp32 accumulators out (gate/up: g and v without SwiGLU; down: fp32 instead of bf16)
 hipError_t launch_gemm_mfma(const GemmArgs& a, bool fp8, bool gateup, int grid, hipStream_t s, bool raw = false);

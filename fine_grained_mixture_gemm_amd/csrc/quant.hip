@@ -4,6 +4,7 @@
 // with saturation.
 #include "common.h"
 #include "kernels.h"
+#include "tiles.h"
 
 namespace moe {
 
@@ -11,10 +12,9 @@ namespace moe {
 // per lane; one 256-thread block covers 32 groups (4096 columns of one row, or several rows when cols is
 // smaller).
 template <typename TX>
-__global__ __launch_bounds__(256) void quant_act_1x128(const TX* __restrict__ x, int rows, int cols,
-                                                       uint8_t* __restrict__ q, float* __restrict__ scales) {
+__device__ __forceinline__ void quant_act_group(const TX* __restrict__ x, int rows, int cols, uint8_t* __restrict__ q,
+                                                float* __restrict__ scales, long long group) {
   const int groups_per_row = cols / 128;
-  const long long group = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
   if (group >= (long long)rows * groups_per_row) return;   // 8-lane groups exit together
   const int row = (int)(group / groups_per_row), gc = (int)(group % groups_per_row);
   const int sub = threadIdx.x & 7;
@@ -50,6 +50,26 @@ __global__ __launch_bounds__(256) void quant_act_1x128(const TX* __restrict__ x,
   out.w = f32x4_to_e4m3x4(v[12] * inv, v[13] * inv, v[14] * inv, v[15] * inv);
   *reinterpret_cast<uint4*>(q + base) = out;
   if (sub == 0) scales[(size_t)row * groups_per_row + gc] = s;
+}
+
+template <typename TX>
+__global__ __launch_bounds__(256) void quant_act_1x128(const TX* __restrict__ x, int rows, int cols,
+                                                       uint8_t* __restrict__ q, float* __restrict__ scales) {
+  quant_act_group(x, rows, cols, q, scales, (long long)blockIdx.x * 32 + (threadIdx.x >> 3));
+}
+
+// The forward's bf16 activations before the matrix-core GEMMs: block 0 computes the tile schedule of the
+// two grouped launches (it needs only the dispatch offsets) while the other blocks quantize, 64 groups of
+// 128 elements per 512-thread block; one launch instead of two in a row.
+__global__ __launch_bounds__(512) void quant_act_schedule(const uint16_t* __restrict__ x, int rows, int cols,
+                                                          uint8_t* __restrict__ q, float* __restrict__ scales,
+                                                          SchedArgs sa) {
+  if (blockIdx.x == 0) {
+    schedule_mfma_block(sa.offsets, sa.E, sa.T, sa.bm, sa.nt_r[0], sa.nt_s[0], sa.nt_r[1], sa.nt_s[1], sa.mt_prefix,
+                        sa.xrange, sa.xcount);
+    return;
+  }
+  quant_act_group(x, rows, cols, q, scales, (long long)(blockIdx.x - 1) * 64 + (threadIdx.x >> 3));
 }
 
 // One 256-thread block per 128x128 block: each thread handles 64 elements (half a row).
@@ -141,6 +161,14 @@ hipError_t launch_quant_act(const void* x, bool x_bf16, int rows, int cols, uint
   const unsigned nb = (unsigned)((groups + 31) / 32);
   if (x_bf16) quant_act_1x128<uint16_t><<<nb, 256, 0, s>>>((const uint16_t*)x, rows, cols, q, scales);
   else quant_act_1x128<float><<<nb, 256, 0, s>>>((const float*)x, rows, cols, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_schedule(const void* x, int rows, int cols, uint8_t* q, float* scales, const SchedArgs& sa,
+                                     hipStream_t s) {
+  const long long groups = (long long)rows * (cols / 128);
+  const unsigned nb = 1 + (unsigned)((groups + 63) / 64);
+  quant_act_schedule<<<nb, 512, 0, s>>>((const uint16_t*)x, rows, cols, q, scales, sa);
   return hipGetLastError();
 }
 

@@ -119,23 +119,59 @@ __global__ __launch_bounds__(256) void router_prep_wg(const float* __restrict__ 
   const int e = blockIdx.x;
   const size_t n = (size_t)E * d;
   float s = 0.f;
-  // each thread's elements k = tid, tid + 256, ... in groups of 16, all loads of a group in flight at once;
-  // the squares are added in k order either way
-  constexpr int kG = 16;
-  for (int k0 = threadIdx.x; k0 < d; k0 += 256 * kG) {
-    float v[kG];
+  if (d % 4 == 0) {
+    // 16-byte pieces: thread tid takes pieces p = tid, tid + 256, ... (elements 4p..4p+3), eight pieces
+    // in flight at once; its squares are added in element order
+    constexpr int kG = 8;
+    const int np = d / 4;
+    const float4* w4 = reinterpret_cast<const float4*>(wg + (size_t)e * d);
+    for (int p0 = threadIdx.x; p0 < np; p0 += 256 * kG) {
+      float4 v[kG];
 #pragma unroll
-    for (int q = 0; q < kG; ++q) {
-      const int k = k0 + 256 * q;
-      v[q] = k < d ? wg[(size_t)e * d + k] : 0.f;
+      for (int q = 0; q < kG; ++q) {
+        const int p = p0 + 256 * q;
+        v[q] = p < np ? w4[p] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int q = 0; q < kG; ++q) {
+        const int p = p0 + 256 * q;
+        if (p < np) {
+          const float x[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s = fmaf(x[r], x[r], s);
+          if constexpr (SPLIT) {
+            ushort4 h, m, l;
+            split_bf16x3(x[0], h.x, m.x, l.x);
+            split_bf16x3(x[1], h.y, m.y, l.y);
+            split_bf16x3(x[2], h.z, m.z, l.z);
+            split_bf16x3(x[3], h.w, m.w, l.w);
+            const size_t i = (size_t)e * d + 4 * (size_t)p;
+            *reinterpret_cast<ushort4*>(parts + i) = h;
+            *reinterpret_cast<ushort4*>(parts + n + i) = m;
+            *reinterpret_cast<ushort4*>(parts + 2 * n + i) = l;
+          }
+        }
+      }
     }
+  } else {
+    // each thread's elements k = tid, tid + 256, ... in groups of 16, all loads of a group in flight at
+    // once; the squares are added in k order
+    constexpr int kG = 16;
+    for (int k0 = threadIdx.x; k0 < d; k0 += 256 * kG) {
+      float v[kG];
 #pragma unroll
-    for (int q = 0; q < kG; ++q) {
-      const int k = k0 + 256 * q;
-      if (k < d) {
-        const size_t i = (size_t)e * d + k;
-        s = fmaf(v[q], v[q], s);
-        if constexpr (SPLIT) split_bf16x3(v[q], parts[i], parts[n + i], parts[2 * n + i]);
+      for (int q = 0; q < kG; ++q) {
+        const int k = k0 + 256 * q;
+        v[q] = k < d ? wg[(size_t)e * d + k] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < kG; ++q) {
+        const int k = k0 + 256 * q;
+        if (k < d) {
+          const size_t i = (size_t)e * d + k;
+          s = fmaf(v[q], v[q], s);
+          if constexpr (SPLIT) split_bf16x3(v[q], parts[i], parts[n + i], parts[2 * n + i]);
+        }
       }
     }
   }
