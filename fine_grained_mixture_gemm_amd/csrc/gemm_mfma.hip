@@ -391,12 +391,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_mfma(GemmArgs a) {
         }
         barrier_lds();
         float* OS = shared ? a.out_scale_shared : a.out_scale_routed;
+        // every exchange read comes before the first store: an LDS read placed after a global store waits
+        // for that store to complete (the compiler guards LDS reads that may follow LDS-DMA copies with a
+        // full vector-memory wait), which would put one store round trip per 16-token tile in the epilogue
+        float sj[kTJ], ij[kTJ];
 #pragma unroll
         for (int j = 0; j < kTJ; ++j) {
           const int tok = tok0 + 16 * j + tr;
           const float m = fmaxf(fmaxf(red[tok], red[kBM + tok]), fmaxf(red[2 * kBM + tok], red[3 * kBM + tok]));
-          float s, inv;
-          e4m3_scales(m, s, inv);
+          e4m3_scales(m, sj[j], ij[j]);
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < kTJ; ++j) {
+          const int tok = tok0 + 16 * j + tr;
+          const float s = sj[j], inv = ij[j];
           if (tok < tc.nrows) {
             if (wn == 0 && g == 0) {
               const int os_ld = shared ? a.os_ld_shared : a.os_ld_routed;
