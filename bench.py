@@ -7,8 +7,9 @@ workload has one. Inputs and weights are resident in HBM before timing starts. T
 the V3-shaped layer: T = 8192 tokens, d = 7168, 1 shared + 256 routed SwiGLU experts of inner dim 2048,
 sigmoid affinity + selection bias, top-8, renormalised gates, E4M3 experts with 1x128 / 128x128 scales.
 
-Prints ONE JSON line. `roofline` covers the dominant kernel (the gate/up grouped GEMM), timed live with
-HIP events on the launch stream over the timed steps; `configs` holds the same record for the other
+The step is captured once into a HIP graph and the timed steps are replays of it (`launch`; the eager
+time of the same steps is `eager_ms_per_step`). Prints ONE JSON line. `roofline` covers the dominant kernel
+(the gate/up grouped GEMM), timed live with HIP events on the launch stream over the eager timed steps; `configs` holds the same record for the other
 configurations (the 2B and 16B bf16 layers and the 64-token V3 decode step), each timed in a run of its
 own after the headline; `cpu_baseline` times the float64 CPU oracle on a bounded sample of the headline
 workload on this host, scaled to the whole batch.
@@ -48,6 +49,8 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip timing the E4M3 expert backward")
     ap.add_argument("--no-subconfigs", action="store_true",
                     help="skip the timed runs of the other configurations (2B / 16B bf16 layers, V3 decode step)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the eager steps only (no HIP-graph capture; for profiler runs)")
     ap.add_argument("--sub-steps", type=int, default=300)
     ap.add_argument("--sub-warmup", type=int, default=20)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -315,7 +318,43 @@ def library_record(moe):
             "sha256": hashlib.sha256(open(moe.LIB_PATH, "rb").read()).hexdigest()[:16]}
 
 
-def measure(moe, layers, w, steps, warmup):
+def time_graph_replays(step, stream, steps, warmup):
+    """The same step captured once into a HIP graph (torch.cuda.CUDAGraph) and replayed `steps` times after
+    `warmup` untimed replays: every kernel of the step runs on every replay, on the same resident inputs;
+    what the graph removes is the host's per-launch cost, which bounds small layers (the 2B layer's ~20
+    launches per step take longer on the host than its kernels on the device). Returns (ms per step,
+    None), or (None, message) when capture is not possible, in which case the eager time stands."""
+    import torch
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+    except Exception as e:                       # capture refused: report it and keep the eager timing
+        torch.cuda.synchronize()
+        return None, f"{type(e).__name__}: {e}"[:300]
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del graph
+    return ms, None
+
+
+def measure(moe, layers, w, steps, warmup, graph=True):
     """Build workload w on the device and time `steps` steps after `warmup` untimed ones. Returns the
     record (step time, per-stage times from HIP events on the launch stream, grouped-GEMM rates and
     rooflines) and the device layer, workspace and step outputs for further timings."""
@@ -359,7 +398,9 @@ def measure(moe, layers, w, steps, warmup):
     moe.moe_set_timing_events(None)
     t_end.record(stream)
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / steps
+    eager_ms = t_start.elapsed_time(t_end) / steps
+    graph_ms, graph_err = time_graph_replays(step, stream, steps, warmup) if graph else (None, None)
+    ms = graph_ms if graph_ms is not None else eager_ms
     stage = {}
     for a, b in zip(moe.MARK_NAMES[:-1], moe.MARK_NAMES[1:]):
         ia, ib = moe.MARK_NAMES.index(a), moe.MARK_NAMES.index(b)
@@ -370,7 +411,8 @@ def measure(moe, layers, w, steps, warmup):
     gemm_tflops = (gwork["flops"] + dwork["flops"]) / (gemm_ms * 1e-3) / 1e12
     rec = {
         "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "steps": steps, "warmup": warmup,
-        "ms_per_step": round(ms, 4), "dtype": {"fp8": "fp8_e4m3", "bf16": "bf16", "f32": "f32"}[w.wdt],
+        "ms_per_step": round(ms, 4), "launch": "hip_graph" if graph_ms is not None else "eager",
+        "eager_ms_per_step": round(eager_ms, 4), "dtype": {"fp8": "fp8_e4m3", "bf16": "bf16", "f32": "f32"}[w.wdt],
         "config": {"workload": w.name, "T": w.T, "d_model": w.d, "routed": w.E, "shared": w.Ks, "top_k": w.K,
                    "inter_dim": w.f, "gate": w.gate, "renorm": w.renorm, "weights": w.wdt, "act": w.act,
                    "bias_update": w.gamma is not None},
@@ -386,11 +428,13 @@ def measure(moe, layers, w, steps, warmup):
         "touched_experts": touched,
         "setup_s": round(setup_s, 1),
     }
+    if graph_err is not None:
+        rec["graph_error"] = graph_err
     prof = profiled_traffic(w.name)
     if prof is not None:
         rec["roofline"]["traffic"] = round(prof["gateup"]["traffic_bytes"])
         rec["down_roofline"]["traffic"] = round(prof["down"]["traffic_bytes"])
-    note(f"{w.name}: {ms:.3f} ms per step over {steps} steps, gate/up {stage['gateup']:.3f} ms, "
+    note(f"{w.name}: {ms:.3f} ms per step over {steps} steps ({rec['launch']}; eager {eager_ms:.3f}), gate/up {stage['gateup']:.3f} ms, "
          f"down {stage['down']:.3f} ms (set-up {setup_s:.0f} s)")
     return rec, L, ws
 
@@ -423,7 +467,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    rec, L, ws = measure(moe, layers, w, args.steps, args.warmup)
+    rec, L, ws = measure(moe, layers, w, args.steps, args.warmup, graph=not args.no_graph)
     out = {"metric": METRIC, "value": rec.pop("value"), "unit": rec.pop("unit"), "n_gpus": 1,
            "steps": rec.pop("steps"), "warmup": rec.pop("warmup"), "ms_per_step": rec.pop("ms_per_step"),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": rec.pop("dtype"),
@@ -444,7 +488,8 @@ def main():
         for name in SUB_WORKLOADS:
             if name == w.name:
                 continue
-            sub, Ls, wss = measure(moe, layers, configs.WORKLOADS[name], args.sub_steps, args.sub_warmup)
+            sub, Ls, wss = measure(moe, layers, configs.WORKLOADS[name], args.sub_steps, args.sub_warmup,
+                                   graph=not args.no_graph)
             out["configs"][name] = sub
             del Ls, wss
             torch.cuda.empty_cache()

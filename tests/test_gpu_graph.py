@@ -133,3 +133,51 @@ def test_forward_graph_replays_match_eager(name):
     graph.replay()
     torch.cuda.synchronize()
     _check(outs, ref, f"{name} replay on the first batch again")
+
+
+def test_step_with_bias_update_graph_replays_match_eager():
+    """The timed step of the decode workload (forward, then a copy of the bias and one bias update into the
+    copy) captured as one graph: every replay gives the eager step's h, routing, counts and updated bias bit
+    for bit, and the bias the forward reads is never changed by a replay."""
+    w = CASES["fp8_decode"].replace(name="graph_fp8_decode_bias", gamma=0.001)
+    print(f"[case] graph step with bias update T={w.T}", flush=True)
+    g = H.build(w)
+    layer = _tiled_layer(g)
+    bias = g.t["bias"]
+    bias0 = bias.clone()
+    ws = H.workspace(g, poison=True)
+    outs = _outputs(g)
+    bias_next = torch.empty_like(bias)
+
+    def step():
+        moe.moe_forward(g.cfg, layer, g.t["u"], bias, *outs, ws)
+        bias_next.copy_(bias)
+        moe.moe_update_bias(g.cfg, outs[2], w.gamma, bias_next)
+
+    _poison(outs)
+    step()
+    torch.cuda.synchronize()
+    ref = tuple(x.clone() for x in outs)
+    ref_bias = bias_next.clone()
+    assert not torch.equal(ref_bias, bias0), "the update left every bias unchanged: no load differs from the mean"
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        _poison(outs)
+        bias_next.fill_(float("nan"))
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _check(outs, ref, f"bias step replay {rep}")
+        assert _same(bias_next, ref_bias), f"replay {rep}: updated bias differs from the eager step"
+        assert _same(bias, bias0), f"replay {rep}: the forward's bias changed"
