@@ -3,7 +3,8 @@
 // summed in fp32 in that order (k ascending = expert ascending), rounded once to the output dtype.
 // A pair that dispatch dropped (row_of = -1: no routed expert, or a repeated one) adds nothing.
 // One block per token (d/16 threads rounded up to whole waves, 64 to 1024); each thread reads and writes
-// 16-byte pieces of the rows, so every row access is a contiguous, coalesced sweep.
+// 16-byte pieces of the rows, so every row access is a contiguous, coalesced sweep. A thread issues all
+// the loads of a piece (u, the shared row, up to 8 routed rows) before it adds any of them.
 //
 // Bias update (same report, 3.3): b_i - gamma for an overloaded expert, b_i + gamma for an
 // underloaded one, unchanged at the mean load; decided in integers as counts_i * E against T * K.
@@ -14,7 +15,7 @@
 
 namespace moe {
 
-constexpr int kCombineMaxK = 8;   // routed rows held in registers at once (bf16 expert outputs)
+constexpr int kCombineMaxK = 8;   // routed rows held in registers at once
 
 // BF16: u and h are bf16 (else fp32); YBF16: the expert outputs are bf16 (else fp32).
 template <bool BF16, bool YBF16>
@@ -51,36 +52,55 @@ __global__ __launch_bounds__(1024) void combine_rows(const void* __restrict__ u_
     return bf ? bf16_to_f32(static_cast<const uint16_t*>(p)[off]) : static_cast<const float*>(p)[off];
   };
   const int nvec = vec ? d / 8 : 0;
+  // 16-byte words per 8 elements of u / h and of the expert outputs
+  constexpr int UW = BF16 ? 1 : 2, YW = YBF16 ? 1 : 2;
+  auto unpack = [](const uint4 (&w)[2], bool bf, float (&v)[8]) {
+    const uint32_t x[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v[i] = bf ? __uint_as_float(i & 1 ? x[i / 2] & 0xFFFF0000u : x[i / 2] << 16) : __uint_as_float(x[i]);
+  };
+  auto words = [](const void* p, size_t byte_off, int n, uint4 (&w)[2]) {
+    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(p) + byte_off);
+    w[0] = q[0];
+    if (n > 1) w[1] = q[1];
+  };
   for (int c = threadIdx.x; c < nvec; c += blockDim.x) {
     const size_t col = (size_t)c * 8;
     float acc[8], y[8];
-    load8(u_, BF16, (size_t)t * d + col, acc);
-    if (ys_) {
-      load8(ys_, YBF16, (size_t)t * d + col, y);
+    if (K <= kCombineMaxK) {
+      // every load of this piece (u, the shared row, the routed rows) is issued before any of them is used,
+      // so a piece waits for one memory round trip; the sums keep their order
+      uint4 ru[2] = {}, rs[2] = {}, ry[kCombineMaxK][2] = {};
+      int rows[kCombineMaxK];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += y[i];
-    }
-    if (YBF16 && K <= kCombineMaxK) {
-      // every routed row's piece is requested before the first is used (K loads in flight), then the
-      // rows are added in order
-      uint4 raw[kCombineMaxK];
+      for (int k = 0; k < kCombineMaxK; ++k) rows[k] = k < K ? s_row[k] : -1;
+      words(u_, ((size_t)t * d + col) * (BF16 ? 2 : 4), UW, ru);
+      if (ys_) words(ys_, ((size_t)t * d + col) * (YBF16 ? 2 : 4), YW, rs);
 #pragma unroll
       for (int k = 0; k < kCombineMaxK; ++k)
-        if (k < K && s_row[k] >= 0)
-          raw[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(yr_) + (size_t)s_row[k] * d + col);
+        if (rows[k] >= 0) words(yr_, ((size_t)rows[k] * d + col) * (YBF16 ? 2 : 4), YW, ry[k]);
+      unpack(ru, BF16, acc);
+      if (ys_) {
+        unpack(rs, YBF16, y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += y[i];
+      }
 #pragma unroll
       for (int k = 0; k < kCombineMaxK; ++k) {
-        if (k >= K) break;
-        if (s_row[k] < 0) continue;
+        if (rows[k] < 0) continue;
         const float g = s_g[k];
-        const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+        unpack(ry[k], YBF16, y);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(g, __uint_as_float(w[i] << 16), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(g, __uint_as_float(w[i] & 0xFFFF0000u), acc[2 * i + 1]);
-        }
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, y[i], acc[i]);
       }
     } else {
+      load8(u_, BF16, (size_t)t * d + col, acc);
+      if (ys_) {
+        load8(ys_, YBF16, (size_t)t * d + col, y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += y[i];
+      }
       for (int k = 0; k < K; ++k) {
         if (s_row[k] < 0) continue;
         load8(yr_, YBF16, (size_t)s_row[k] * d + col, y);
