@@ -45,7 +45,7 @@ SMALL = {
     "bf16_k12": W["dsmoe2b_bf16"].replace(name="bf16_k12", T=150, d=256, E=24, K=12, f=128),
     "bf16_k16_sigmoid": W["dsmoe2b_bf16"].replace(name="bf16_k16_sigmoid", T=90, d=256, E=20, K=16, f=128,
                                                    gate="sigmoid_bias", renorm=True, bias_range=0.1, zipf=None),
-    # enough tokens for the MFMA router logits (T * E >= 2^17) with an expert count that is not a multiple
+    # enough tokens for the MFMA router logits (T * E >= 2^16) with an expert count that is not a multiple
     # of its 64-expert blocks, a ragged last token block, and d = 1024 split into two slices (the expert
     # inner dim 512: with d = 1024 and f = 128 the bf16 rounding of the routed sum reaches the tolerance)
     "bf16_mfma_router_e63": W["dsmoe2b_bf16"].replace(name="bf16_mfma_router_e63", T=2100, d=1024, E=63, K=7,
