@@ -57,6 +57,9 @@ SMALL = {
     "fp8_heavy_tail": W["v3_fp8"].replace(name="fp8_heavy_tail", T=300, d=512, E=20, K=4, u_tail=True),
     "bf16_heavy_tail_mfma_router": W["dsmoe2b_bf16"].replace(name="bf16_heavy_tail_mfma_router", T=2100, d=1024,
                                                              E=63, K=7, f=512, u_tail=True),
+    # the largest d_model the library takes (8192: the fp64 recheck holds a whole centroid row, 32 elements
+    # per thread): router, recheck, 32 K stages of the tiled bf16 kernel and the combine at that width
+    "bf16_max_d": W["dsmoe2b_bf16"].replace(name="bf16_max_d", T=300, d=8192, E=8, K=2, f=512),
 }
 
 
